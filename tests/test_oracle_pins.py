@@ -1,0 +1,292 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+* hand-worked examples derived from the pages' definition (tests/golden/);
+* the closed form: with log_eps = -inf nothing is ever flagged and the output is naive dense
+  softmax attention; with any fixed mask the output is block-masked softmax attention;
+* brute force on tiny inputs, recomputing every running maximum from scratch in pure Python;
+* invariants: monotone masks, normalisation (V = 1 gives 1), the first visited tile is never
+  flagged, flagged tiles carry little softmax mass, exemptions, head permutation, determinism.
+"""
+import json
+import math
+import os
+import random
+
+import numpy as np
+import pytest
+
+from oracle import bits_to_mask, empty_mask, lite_attn_step_ref, mask_geometry, mask_to_bits
+import pyref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _one_head(x):
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+# ------------------------------------------------------------------ golden, hand-worked
+def test_golden_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "qk_skip_worked_example.json")))
+    q = _one_head(g["q"])
+    k = _one_head(g["k"])
+    v = _one_head(np.ones((g["seq_len"], 1)))
+    for case in g["cases"]:
+        mask = np.asarray(case["mask_in"], dtype=np.uint32)[None, None]
+        res = lite_attn_step_ref(q, k, v, mask, tile_q=g["tile_q"], tile_k=g["tile_k"],
+                                 softmax_scale=case["scale"], log_eps=case.get("log_eps", g["log_eps"]),
+                                 step=case["step"], order=case["order"],
+                                 dense_prefix=case["dense_prefix"])
+        got = res.mask_next[0, 0]
+        assert got.tolist() == case["mask_out"], case["name"]
+        new = mask_to_bits(res.mask_next, 5) & ~mask_to_bits(mask, 5)
+        for i, fl in enumerate(case["flags"]):
+            assert sorted(np.nonzero(new[0, 0, i])[0].tolist()) == fl, (case["name"], i)
+        if "margins_row0" in case:
+            m = res.margins[0, 0, 0]
+            exp = case["margins_row0"]
+            assert math.isinf(m[0]) and m[0] > 0
+            np.testing.assert_allclose(m[1:], exp[1:], rtol=0, atol=1e-12)
+
+
+def test_golden_bit_layout():
+    g = json.load(open(os.path.join(GOLDEN, "mask_bit_layout.json")))
+    n = g["seq_len"]
+    kv = np.full((n, 1), g["k_default"])
+    for c, val in g["k_special"].items():
+        kv[int(c), 0] = val
+    q = _one_head(np.ones((n, 1)))
+    k = _one_head(kv)
+    v = _one_head(np.zeros((n, 1)))
+    res = lite_attn_step_ref(q, k, v, empty_mask(1, 1, n, g["tile_q"], g["tile_k"]),
+                             tile_q=g["tile_q"], tile_k=g["tile_k"], softmax_scale=1.0,
+                             log_eps=g["log_eps"], step=0, order="asc")
+    assert res.mask_next[0, 0, 0].tolist() == g["mask_out"]
+
+
+# ------------------------------------------------------------------ closed forms
+def _rand(rng, n, d, spread=1.0):
+    return (rng.standard_normal((n, d)) * spread).tolist()
+
+
+@pytest.mark.parametrize("n,d,tq,tk", [(13, 3, 4, 3), (16, 2, 8, 8), (7, 5, 3, 2), (1, 1, 1, 1)])
+def test_no_skip_equals_naive_dense_attention(n, d, tq, tk):
+    rng = np.random.default_rng(n * 100 + d)
+    q, k, v = _rand(rng, n, d, 2.0), _rand(rng, n, d, 2.0), _rand(rng, n, d)
+    scale = 0.7
+    res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), empty_mask(1, 1, n, tq, tk),
+                             tile_q=tq, tile_k=tk, softmax_scale=scale, log_eps=-math.inf,
+                             step=1, order="alt")
+    want = pyref.masked_attention(q, k, v, [[True] * n for _ in range(n)], scale)
+    np.testing.assert_allclose(res.out[0, 0], np.array(want), rtol=1e-12, atol=1e-12)
+    assert not res.mask_next.any()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fixed_mask_equals_block_masked_attention(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(5, 30))
+    d = int(rng.integers(1, 5))
+    tq = int(rng.integers(1, 9))
+    tk = int(rng.integers(1, 9))
+    q, k, v = _rand(rng, n, d, 1.5), _rand(rng, n, d, 1.5), _rand(rng, n, 3)
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    bits = rng.random((tqn, tkn)) < 0.4
+    mask = bits_to_mask(bits)[None, None]
+    res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, tile_q=tq, tile_k=tk,
+                             softmax_scale=1.3, log_eps=-math.inf, step=0, order="asc")
+    allowed = [[not bits[r // tq, c // tk] for c in range(n)] for r in range(n)]
+    want = pyref.masked_attention(q, k, v, allowed, 1.3)
+    np.testing.assert_allclose(res.out[0, 0], np.array(want), rtol=1e-12, atol=1e-12)
+    # rows whose tile allows nothing are zero
+    for i in range(tqn):
+        if bits[i].all():
+            assert np.all(res.out[0, 0, i * tq:(i + 1) * tq] == 0)
+
+
+# ------------------------------------------------------------------ brute force on tiny inputs
+@pytest.mark.parametrize("seed", range(40))
+def test_mask_update_matches_brute_force(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(4, 40))
+    d = int(rng.integers(1, 5))
+    tq = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    tk = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    scale = float(rng.choice([1.0, 0.5, 2.5]))
+    log_eps = float(rng.choice([-0.5, -2.0, -4.0, -8.0]))
+    step = int(rng.integers(0, 4))
+    order = str(rng.choice(["asc", "alt"]))
+    prefix = int(rng.choice([0, 0, 3]))
+    q, k, v = _rand(rng, n, d, 2.0), _rand(rng, n, d, 2.0), _rand(rng, n, 2)
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    skipped = rng.random((tqn, tkn)) < float(rng.choice([0.0, 0.3]))
+    mask = bits_to_mask(skipped)[None, None]
+    res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, tile_q=tq, tile_k=tk,
+                             softmax_scale=scale, log_eps=log_eps, step=step, order=order,
+                             dense_prefix=prefix)
+    descending = order == "alt" and step % 2 == 1
+    flags, margins = pyref.brute_flags(q, k, skipped.tolist(), tq, tk, scale, log_eps,
+                                       descending, prefix)
+    got_new = mask_to_bits(res.mask_next, tkn)[0, 0] & ~skipped
+    for i in range(tqn):
+        for j in range(tkn):
+            if skipped[i, j]:
+                assert math.isnan(res.margins[0, 0, i, j])
+                continue
+            mb = margins[i][j]
+            mo = res.margins[0, 0, i, j]
+            if math.isinf(mb):
+                assert mo == mb
+            else:
+                assert abs(mo - mb) <= 1e-9 * max(1.0, abs(mb))
+                if abs(mb) < 1e-9:
+                    continue
+            assert bool(got_new[i, j]) == flags[i][j], (i, j, mb)
+    # old bits are kept
+    assert np.all(mask_to_bits(res.mask_next, tkn)[0, 0] | ~skipped)
+
+
+# ------------------------------------------------------------------ invariants over chains
+def _chain_inputs(seed, n, d, steps, spread=1.2):
+    rng = np.random.default_rng(seed)
+    base_q = rng.standard_normal((2, 3, n, d)) * spread
+    base_k = rng.standard_normal((2, 3, n, d)) * spread
+    v = rng.standard_normal((2, 3, n, d))
+    out = []
+    for t in range(steps):
+        out.append((base_q + 0.05 * rng.standard_normal(base_q.shape),
+                    base_k + 0.05 * rng.standard_normal(base_k.shape), v))
+    return out
+
+
+@pytest.mark.parametrize("order", ["asc", "alt"])
+def test_chain_monotone_normalised_first_tile_kept(order):
+    n, d, tq, tk, steps = 70, 8, 16, 8, 5
+    scale, eps = 1.0, [-math.inf, -6.0, -5.0, -4.0, -4.0]
+    inputs = _chain_inputs(7, n, d, steps, spread=1.5)
+    mask = empty_mask(2, 3, n, tq, tk)
+    _, tkn, _ = mask_geometry(n, tq, tk)
+    total_flags = 0
+    for t in range(steps):
+        q, k, v = inputs[t]
+        res = lite_attn_step_ref(q, k, np.ones_like(v), mask, tile_q=tq, tile_k=tk,
+                                 softmax_scale=scale, log_eps=eps[t], step=t, order=order)
+        # normalisation: with V = 1 every output element is 1
+        np.testing.assert_allclose(res.out, 1.0, rtol=0, atol=1e-12)
+        old = mask_to_bits(mask, tkn)
+        new = mask_to_bits(res.mask_next, tkn)
+        assert not np.any(old & ~new), "bits were cleared"
+        total_flags += int((new & ~old).sum())
+        # first visited tile of every row tile is never flagged
+        descending = order == "alt" and t % 2 == 1
+        for idx in np.ndindex(old.shape[:3]):
+            vis = [j for j in (range(tkn - 1, -1, -1) if descending else range(tkn)) if not old[idx][j]]
+            assert vis and not new[idx][vis[0]]
+        if t == 0:
+            assert total_flags == 0  # log_eps = -inf flags nothing
+        mask = res.mask_next
+    assert total_flags > 0  # the case is not vacuous
+
+
+def test_flagged_tiles_carry_little_mass():
+    """A tile flagged at step t holds less than tile_k * exp(log_eps) of any of its rows'
+    softmax mass at step t (the running max only grows and the normaliser is >= 1)."""
+    n, d, tq, tk = 48, 3, 8, 4
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((n, d)) * 2
+    k = rng.standard_normal((n, d)) * 2
+    log_eps = -3.0
+    for order, step in (("asc", 0), ("alt", 1)):
+        res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(np.zeros((n, 1))),
+                                 empty_mask(1, 1, n, tq, tk), tile_q=tq, tile_k=tk,
+                                 softmax_scale=1.0, log_eps=log_eps, step=step, order=order)
+        s = pyref.scores(q.tolist(), k.tolist(), 1.0)
+        _, tkn, _ = mask_geometry(n, tq, tk)
+        fl = mask_to_bits(res.mask_next, tkn)[0, 0]
+        assert fl.any()
+        for i, j in zip(*np.nonzero(fl)):
+            for r in range(i * tq, min(n, (i + 1) * tq)):
+                mx = max(s[r])
+                z = sum(math.exp(x - mx) for x in s[r])
+                mass = sum(math.exp(s[r][c] - mx) for c in range(j * tk, min(n, (j + 1) * tk))) / z
+                assert mass < tk * math.exp(log_eps)
+
+
+def test_dense_prefix_exemption_and_orders_agree_on_even_steps():
+    inputs = _chain_inputs(11, 50, 4, 1, spread=2.0)
+    q, k, v = inputs[0]
+    tq, tk, prefix = 8, 4, 12
+    mask = empty_mask(2, 3, 50, tq, tk)
+    a = lite_attn_step_ref(q, k, v, mask, tile_q=tq, tile_k=tk, softmax_scale=1.0, log_eps=-2.0,
+                           step=2, order="asc", dense_prefix=prefix)
+    b = lite_attn_step_ref(q, k, v, mask, tile_q=tq, tile_k=tk, softmax_scale=1.0, log_eps=-2.0,
+                           step=2, order="alt", dense_prefix=prefix)
+    assert np.array_equal(a.mask_next, b.mask_next)
+    assert np.array_equal(a.out, b.out)
+    c = lite_attn_step_ref(q, k, v, mask, tile_q=tq, tile_k=tk, softmax_scale=1.0, log_eps=-2.0,
+                           step=3, order="alt", dense_prefix=prefix)
+    for res in (a, c):
+        bits = mask_to_bits(res.mask_next, 13)
+        assert not bits[:, :, :2, :].any()      # row tiles 0, 1 touch tokens < 12
+        assert not bits[:, :, :, :3].any()      # key tiles 0..2 touch tokens < 12
+        assert bits.any()
+    free = lite_attn_step_ref(q, k, v, mask, tile_q=tq, tile_k=tk, softmax_scale=1.0,
+                              log_eps=-2.0, step=3, order="alt")
+    assert mask_to_bits(free.mask_next, 13)[:, :, :, :3].any()  # exemption matters here
+
+
+def test_head_permutation_equivariance_and_determinism():
+    q, k, v = _chain_inputs(5, 40, 4, 1, spread=2.0)[0]
+    mask = bits_to_mask(np.random.default_rng(0).random((2, 3, 5, 10)) < 0.2)
+    kw = dict(tile_q=8, tile_k=4, softmax_scale=1.0, log_eps=-3.0, step=1, order="alt")
+    r1 = lite_attn_step_ref(q, k, v, mask, **kw)
+    r2 = lite_attn_step_ref(q, k, v, mask, **kw)
+    assert np.array_equal(r1.out, r2.out) and np.array_equal(r1.mask_next, r2.mask_next)
+    perm = [2, 0, 1]
+    rp = lite_attn_step_ref(q[:, perm], k[:, perm], v[:, perm], mask[:, perm], **kw)
+    assert np.array_equal(rp.out, r1.out[:, perm])
+    assert np.array_equal(rp.mask_next, r1.mask_next[:, perm])
+    bp = lite_attn_step_ref(q[::-1], k[::-1], v[::-1], mask[::-1], **kw)
+    assert np.array_equal(bp.mask_next, r1.mask_next[::-1])
+
+
+def test_nan_scores_never_flag_and_log_eps_zero():
+    n, d = 16, 2
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((n, d)) * 3
+    k = rng.standard_normal((n, d)) * 3
+    qn = q.copy()
+    qn[5, 0] = np.nan
+    kw = dict(tile_q=8, tile_k=2, softmax_scale=1.0, step=0, order="asc")
+    r = lite_attn_step_ref(_one_head(qn), _one_head(k), _one_head(k), empty_mask(1, 1, n, 8, 2),
+                           log_eps=-0.1, **kw)
+    assert not mask_to_bits(r.mask_next, 8)[0, 0, 0].any()   # row tile 0 holds the NaN row
+    # log_eps = 0 flags exactly the tiles that do not raise any row's running maximum
+    r0 = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(k), empty_mask(1, 1, n, 8, 2),
+                            log_eps=0.0, **kw)
+    s = np.array(pyref.scores(q.tolist(), k.tolist(), 1.0))
+    for i in range(2):
+        rows = s[i * 8:(i + 1) * 8]
+        run = np.full(8, -np.inf)
+        for j in range(8):
+            mt = rows[:, 2 * j:2 * j + 2].max(axis=1)
+            want = bool(np.all(mt < run))
+            assert bool(mask_to_bits(r0.mask_next, 8)[0, 0, i, j]) == want
+            run = np.maximum(run, mt)
+
+
+def test_rejects_bad_arguments_and_empty_inputs():
+    q = np.zeros((1, 1, 4, 2))
+    m = empty_mask(1, 1, 4, 2, 2)
+    with pytest.raises(ValueError):
+        lite_attn_step_ref(q, q, q, m, tile_q=2, tile_k=2, softmax_scale=1.0, log_eps=0.5, step=0)
+    with pytest.raises(ValueError):
+        lite_attn_step_ref(q, q, q, m, tile_q=2, tile_k=2, softmax_scale=1.0, log_eps=float("nan"),
+                           step=0)
+    with pytest.raises(ValueError):
+        lite_attn_step_ref(q, q, q, m, tile_q=2, tile_k=2, softmax_scale=1.0, log_eps=-1.0, step=0,
+                           order="desc")
+    e = np.zeros((1, 1, 0, 2))
+    r = lite_attn_step_ref(e, e, e, empty_mask(1, 1, 0, 2, 2), tile_q=2, tile_k=2,
+                           softmax_scale=1.0, log_eps=-1.0, step=0)
+    assert r.out.shape == (1, 1, 0, 2) and r.mask_next.shape == (1, 1, 0, 0)
