@@ -1,0 +1,153 @@
+/*
+ * lite_attn.h - C ABI of an MI355X (gfx950) implementation of LiteAttention's hot path:
+ * tiled self-attention with an embedded QK-Skip test and a persistent skip mask that
+ * carries across denoising steps.
+ *
+ * Method: "LiteAttention: Temporal Sparse Attention for Diffusion Transformers"
+ * (page 1, sections "Core Concept", "Architecture Overview"; page 2, abstract).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors q, k, v and out have logical shape [B][H][N][D] with element strides
+ *   (stride_b, stride_h, stride_n) and a contiguous last dimension; all four share the
+ *   strides given in lite_attn_config. They are device pointers owned by the caller.
+ * - The skip mask is a caller-owned device array of uint32 words, shape [B][H][Tq][W] with
+ *   Tq = ceil(N / tile_q), Tk = ceil(N / tile_k), W = ceil(Tk / 32). Key tile j of query
+ *   tile i of head (b, h) is bit (j % 32) of word mask[b][h][i][j / 32]; a set bit means
+ *   "skip". Bits at positions >= Tk of a row's last word are reserved: they must be zero and
+ *   are never read or changed. Keep one mask per attention call site (per layer, per
+ *   guidance branch) and pass it to every denoising step of a generation.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream). All device work
+ *   is enqueued asynchronously on it; nothing here synchronises with the host. Errors that
+ *   happen during kernel execution surface at the caller's next synchronisation.
+ * - Return values are lite_attn_status codes. No C++ exception crosses this interface.
+ *   The message for the most recent failing call on the calling thread is available from
+ *   lite_attn_last_error().
+ * - A handle holds only the validated configuration; it owns no device memory. Steps on the
+ *   same handle may run concurrently on different streams when their out and mask buffers
+ *   differ.
+ */
+#ifndef LITE_ATTN_H
+#define LITE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LITE_ATTN_ABI_VERSION 1
+
+typedef enum lite_attn_status {
+  LITE_ATTN_OK = 0,
+  LITE_ATTN_ERR_INVALID_ARG = 1,  /* bad pointer, alignment, size, NaN/positive budget ... */
+  LITE_ATTN_ERR_UNSUPPORTED = 2,  /* valid request, but no kernel is built for it */
+  LITE_ATTN_ERR_HIP = 3,          /* a HIP runtime call failed (launch, device query) */
+  LITE_ATTN_ERR_NO_MEMORY = 4     /* host allocation of the handle failed */
+} lite_attn_status;
+
+typedef enum lite_attn_dtype {
+  LITE_ATTN_BF16 = 0,  /* q, k, v, out are bfloat16; MFMA in bf16 with fp32 accumulation */
+  LITE_ATTN_FP32 = 1   /* q, k, v, out are float32; MFMA in fp32 */
+} lite_attn_dtype;
+
+typedef enum lite_attn_order {
+  /* Key tiles of a query tile are visited in ascending index order at every step. */
+  LITE_ATTN_ORDER_ASC = 0,
+  /* Ascending on even steps, descending on odd steps. The QK-Skip test compares a tile with
+   * the maximum over tiles visited before it, so alternating the direction lets tiles on both
+   * sides of a query's high-score region be flagged. */
+  LITE_ATTN_ORDER_ALT = 1
+} lite_attn_order;
+
+typedef struct lite_attn_config {
+  int32_t abi_version;   /* must be LITE_ATTN_ABI_VERSION */
+  int32_t batch;         /* B >= 0 */
+  int32_t heads;         /* H >= 0 */
+  int32_t seq_len;       /* N >= 0; tokens per head (queries and keys: self-attention) */
+  int32_t head_dim;      /* D: 64 or 128 */
+  int32_t tile_q;        /* query rows per tile: 64 or 128 */
+  int32_t tile_k;        /* keys per tile: 64 */
+  int32_t dtype;         /* lite_attn_dtype; in and out share it */
+  float softmax_scale;   /* > 0; a value <= 0 selects 1/sqrt(head_dim) */
+  int32_t order;         /* lite_attn_order */
+  int32_t dense_prefix;  /* tokens [0, dense_prefix) keep dense attention: a tile whose rows
+                            or columns touch them is never flagged. 0 = off; <= seq_len */
+  int64_t stride_b;      /* element strides shared by q, k, v, out; all three zero selects */
+  int64_t stride_h;      /* the contiguous layout [B][H][N][D]. Each must be a multiple of */
+  int64_t stride_n;      /* 8 elements (16 bytes) so that rows stay 16-byte aligned.       */
+} lite_attn_config;
+
+typedef struct lite_attn_s* lite_attn_t;
+
+/* Validate `cfg` and create a handle (host memory only; no device call).
+ * LiteAttention, page 1 "Architecture Overview": the Skip-Mask bitmask and QK-Skip.
+ * Returns INVALID_ARG for NULL arguments, a wrong abi_version, negative sizes, strides that
+ * are not multiples of 8 elements, or dense_prefix outside [0, seq_len]; UNSUPPORTED for a
+ * head_dim / tile / dtype combination without a kernel or for Tk > 4096 (N > 262144 with
+ * 64-key tiles). On failure *out is set to NULL. */
+int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out);
+
+/* Release a handle. NULL is accepted. Returns OK. */
+int lite_attn_destroy(lite_attn_t handle);
+
+/* Bytes of the skip mask for this handle: B * H * Tq * W * 4 (0 for a NULL handle). */
+size_t lite_attn_mask_bytes(lite_attn_t handle);
+
+/* Mask geometry (Tq, Tk, W) of this handle. Any output pointer may be NULL. */
+int lite_attn_mask_geometry(lite_attn_t handle, int32_t* tiles_q, int32_t* tiles_k,
+                            int32_t* words_per_row);
+
+/* One denoising step of attention over all (b, h), using and updating the skip mask.
+ *
+ * LiteAttention, page 1 "Core Concept" (tiles flagged when their local maximum QK score is
+ * far below the cumulative maximum; the mask carries across steps) and "Architecture
+ * Overview" (bitmask, QK-Skip, per-step error budgets, skip logic inside the FlashAttention
+ * softmax pipeline, persistent propagation); page 2 abstract (decisions made early and
+ * propagated forward).
+ *
+ * For every query tile i of every head, key tiles whose mask bit is set are skipped: their
+ * K/V are not loaded and no score is computed. The remaining tiles are visited in this
+ * step's order (see lite_attn_order; `step` selects the parity) and out receives exact
+ * softmax attention over them (scale = softmax_scale), rows with no visited tile receive 0.
+ * Each visited tile j is tested: with mt[r] its scaled row maxima and m[r] the running row
+ * maxima over tiles visited before it, the tile is flagged when mt[r] - m[r] < log_eps_t for
+ * every valid row r of the tile and the tile is not exempt (dense_prefix). Flagged bits are
+ * OR-ed into `mask` when the query tile finishes (they take effect from the next step); no
+ * bit is ever cleared by this call.
+ *
+ * q, k, v: read-only device tensors (see conventions); out: device tensor written for every
+ * valid row, must not alias q, k or v; mask: device words read and updated in place.
+ * log_eps_t: the step's error budget in natural-log units, in [-inf, 0]; -inf flags nothing.
+ * step: the denoising step index (>= 0), used only for the traversal parity.
+ * Pointers must be 16-byte aligned (mask: 4-byte). Returns INVALID_ARG for NULL or misaligned
+ * pointers, out aliasing an input, NaN or positive log_eps_t, negative step; HIP when the
+ * launch fails. A configuration with B*H*N == 0 returns OK without launching anything. */
+int lite_attn_step(lite_attn_t handle, const void* q, const void* k, const void* v, void* out,
+                   uint32_t* mask, float log_eps_t, int32_t step, void* stream);
+
+/* Clear every word of `mask` (a new generation starts dense). LiteAttention, page 1
+ * "Architecture Overview": decisions persist until the attention distribution shifts; this
+ * is the explicit way to drop them. Uses a fill kernel (no memset node), so it may be
+ * recorded into a HIP graph. Returns INVALID_ARG for a NULL handle or mask. */
+int lite_attn_reset_mask(lite_attn_t handle, uint32_t* mask, void* stream);
+
+/* Count skipped tiles per head: counts[b * H + h] = number of set bits (reserved bits
+ * excluded) in mask[b][h]. `counts` is a device array of B*H uint32 words written on `stream`.
+ * The skipped-tile fraction of the step that uses this mask is sum(counts) / (B*H*Tq*Tk).
+ * Returns INVALID_ARG for NULL pointers. */
+int lite_attn_mask_popcount(lite_attn_t handle, const uint32_t* mask, uint32_t* counts,
+                            void* stream);
+
+/* Static English name of a status code. */
+const char* lite_attn_status_string(int status);
+
+/* Message describing the most recent failure on the calling thread ("" if none). */
+const char* lite_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LITE_ATTN_H */

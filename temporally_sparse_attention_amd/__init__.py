@@ -1,0 +1,79 @@
+"""MI355X (gfx950) implementation of LiteAttention's hot path.
+
+Tiled self-attention with an embedded QK-Skip test and a persistent skip bitmask carried
+across denoising steps ("LiteAttention: Temporal Sparse Attention for Diffusion
+Transformers", page 1 "Core Concept" and "Architecture Overview"). The computation runs in
+liblite_attn.so (hand-written HIP kernels behind a C ABI, include/lite_attn.h); this package
+is a thin binding with the same names plus a small convenience wrapper.
+"""
+from __future__ import annotations
+
+from .binding import (  # noqa: F401
+    ABI_VERSION,
+    EXPORTS,
+    LIB_PATH,
+    Handle,
+    LiteAttnError,
+    lite_attn_create,
+    lite_attn_destroy,
+    lite_attn_last_error,
+    lite_attn_mask_bytes,
+    lite_attn_mask_geometry,
+    lite_attn_mask_popcount,
+    lite_attn_reset_mask,
+    lite_attn_status_string,
+    lite_attn_step,
+    make_config,
+)
+from .schedule import ErrorBudgetSchedule  # noqa: F401
+
+
+class LiteAttention:
+    """One attention call site: a handle plus helpers to allocate and inspect its mask.
+
+    att = LiteAttention(B, H, N, D, tile_q=128, dtype="bf16", softmax_scale=1.0)
+    mask = att.new_mask(device)            # zeroed skip mask (a fresh generation)
+    for t, log_eps in enumerate(schedule):
+        att.step(q_t, k_t, v, out, mask, log_eps, t)
+    """
+
+    def __init__(self, batch: int, heads: int, seq_len: int, head_dim: int, **kw):
+        self.handle = lite_attn_create(batch, heads, seq_len, head_dim, **kw)
+
+    @property
+    def mask_shape(self):
+        return self.handle.mask_shape
+
+    @property
+    def tiles(self):
+        return self.handle.tiles_q, self.handle.tiles_k
+
+    def new_mask(self, device, stream=None):
+        import torch
+        mask = torch.empty(self.mask_shape, dtype=torch.int32, device=device)
+        if mask.numel():
+            lite_attn_reset_mask(self.handle, mask, stream)
+        return mask
+
+    def reset_mask(self, mask, stream=None):
+        lite_attn_reset_mask(self.handle, mask, stream)
+
+    def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None):
+        lite_attn_step(self.handle, q, k, v, out, mask, log_eps_t, step, stream)
+
+    def popcount(self, mask, counts=None, stream=None):
+        """Per-head skipped-tile counts (device int32 [B*H]); asynchronous."""
+        import torch
+        c = self.handle.cfg
+        if counts is None:
+            counts = torch.empty(c.batch * c.heads, dtype=torch.int32, device=mask.device)
+        lite_attn_mask_popcount(self.handle, mask, counts, stream)
+        return counts
+
+    def skipped_fraction(self, mask) -> float:
+        """Skipped-tile fraction of a mask (synchronises with the host)."""
+        c = self.handle.cfg
+        total = c.batch * c.heads * self.handle.tiles_q * self.handle.tiles_k
+        if total == 0:
+            return 0.0
+        return float(self.popcount(mask).to("cpu").long().sum().item()) / total

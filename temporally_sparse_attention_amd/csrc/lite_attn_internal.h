@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lite_attn {
+
+constexpr int kTileK = 64;          // keys per tile (two 32-key MFMA blocks)
+constexpr int kMaxTilesK = 4096;    // visiting list capacity per query tile (LDS)
+constexpr int kMaxWords = kMaxTilesK / 32;
+
+// Everything one forward launch needs. Strides are in elements.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  uint32_t* mask;
+  int64_t sb, sh, sn;
+  int B, H, N;
+  int Tq, Tk, W;
+  float scale;        // softmax scale (natural-log units)
+  float scale_log2;   // scale * log2(e), for exp2-based softmax
+  float log_eps;      // QK-Skip budget in natural-log units (may be -inf)
+  int descending;     // traversal direction of this step
+  int dense_prefix;   // tokens [0, dense_prefix) are exempt from flagging
+};
+
+using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
+
+// Launcher for (dtype, head_dim, tile_q) or nullptr when no kernel is built for it.
+// dtype: 0 = bf16, 1 = fp32.
+FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q);
+
+hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream);
+hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,
+                                int Tq, int Tk, int W, hipStream_t stream);
+
+}  // namespace lite_attn

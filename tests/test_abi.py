@@ -1,0 +1,135 @@
+"""The C-ABI library: it loads without a GPU, exports what include/lite_attn.h declares, and
+its host-side validation returns the documented status codes (no device call is made)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import temporally_sparse_attention_amd as tsa
+from temporally_sparse_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lite_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lite_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                        text=True).stdout
+    exported = set(re.findall(r" T (lite_attn_\w+)", nm))
+    assert set(declared_functions()) <= exported
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "lite_attn.h"\nint main(void){ lite_attn_config c = {0};'
+                   ' (void)c; return (int)sizeof(lite_attn_t) == 0; }\n')
+    for compiler, flags in (("gcc", ["-std=c99"]), ("g++", ["-x", "c++", "-std=c++17"])):
+        r = subprocess.run([compiler, *flags, "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            "-c", str(src), "-o", str(tmp_path / "use.o")], capture_output=True,
+                           text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_config_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "off.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lite_attn.h"\n'
+                   'int main(void){ printf("%zu %zu %zu %zu\\n", sizeof(lite_attn_config),'
+                   ' offsetof(lite_attn_config, softmax_scale), offsetof(lite_attn_config, dense_prefix),'
+                   ' offsetof(lite_attn_config, stride_b)); return 0; }\n')
+    exe = tmp_path / "off"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
+    c = binding.LiteAttnConfig
+    assert [int(x) for x in got] == [ctypes.sizeof(c), c.softmax_scale.offset,
+                                     c.dense_prefix.offset, c.stride_b.offset]
+
+
+def _status(fn):
+    try:
+        fn()
+    except tsa.LiteAttnError as e:
+        return e.status
+    return binding.OK
+
+
+def test_create_validation():
+    ok = lambda **kw: (lambda: tsa.lite_attn_create(1, 2, 1000, 128, **kw))
+    assert _status(ok()) == binding.OK
+    assert _status(ok(dtype="fp32", tile_q=64)) == binding.OK
+    assert _status(lambda: tsa.lite_attn_create(1, 2, 1000, 96)) == binding.ERR_UNSUPPORTED
+    assert _status(ok(tile_k=128)) == binding.ERR_UNSUPPORTED
+    assert _status(ok(tile_q=32)) == binding.ERR_UNSUPPORTED
+    assert _status(lambda: tsa.lite_attn_create(-1, 2, 1000, 128)) == binding.ERR_INVALID_ARG
+    assert _status(ok(dense_prefix=1001)) == binding.ERR_INVALID_ARG
+    assert _status(ok(dense_prefix=-1)) == binding.ERR_INVALID_ARG
+    assert _status(ok(strides=(0, 0, 100))) == binding.ERR_INVALID_ARG     # not a multiple of 8
+    assert _status(ok(strides=(0, 0, 64))) == binding.ERR_INVALID_ARG      # < head_dim
+    assert _status(lambda: tsa.lite_attn_create(1, 1, 300000, 64, tile_q=128)) == binding.ERR_UNSUPPORTED
+    cfg = tsa.make_config(1, 2, 1000, 128)
+    cfg.abi_version = 99
+    assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=cfg)) == binding.ERR_INVALID_ARG
+    lib = binding.library()
+    assert lib.lite_attn_create(None, None) == binding.ERR_INVALID_ARG
+    assert "NULL" in tsa.lite_attn_last_error()
+
+
+def test_geometry_and_mask_bytes():
+    h = tsa.lite_attn_create(2, 3, 75600, 128, tile_q=128)
+    assert tsa.lite_attn_mask_geometry(h) == (591, 1182, 37)
+    assert tsa.lite_attn_mask_bytes(h) == 2 * 3 * 591 * 37 * 4
+    e = tsa.lite_attn_create(0, 3, 100, 64)
+    assert tsa.lite_attn_mask_bytes(e) == 0
+    assert binding.library().lite_attn_mask_bytes(None) == 0
+
+
+def test_step_host_validation_makes_no_device_call():
+    h = tsa.lite_attn_create(1, 1, 100, 64, tile_q=64)
+    lib = binding.library()
+    p = ctypes.c_void_p(4096)
+    ms = ctypes.c_void_p(4096)
+    st = lambda *a: lib.lite_attn_step(h.ptr, *a)
+    assert st(None, p, p, ctypes.c_void_p(8192), ms, ctypes.c_float(-1.0), 0, None) == binding.ERR_INVALID_ARG
+    assert st(p, p, p, ctypes.c_void_p(8192), ms, ctypes.c_float(0.5), 0, None) == binding.ERR_INVALID_ARG
+    assert st(p, p, p, ctypes.c_void_p(8192), ms, ctypes.c_float(math.nan), 0, None) == binding.ERR_INVALID_ARG
+    assert st(p, p, p, ctypes.c_void_p(8192), ms, ctypes.c_float(-1.0), -1, None) == binding.ERR_INVALID_ARG
+    assert st(p, p, p, ctypes.c_void_p(8200), ms, ctypes.c_float(-1.0), 0, None) == binding.ERR_INVALID_ARG
+    assert st(p, p, p, p, ms, ctypes.c_float(-1.0), 0, None) == binding.ERR_INVALID_ARG  # out aliases
+    assert lib.lite_attn_step(None, p, p, p, p, ms, ctypes.c_float(-1.0), 0, None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_reset_mask(h.ptr, None, None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_mask_popcount(h.ptr, ms, None, None) == binding.ERR_INVALID_ARG
+    # an empty problem is a no-op that needs no pointers
+    e = tsa.lite_attn_create(1, 0, 100, 64, tile_q=64)
+    assert lib.lite_attn_step(e.ptr, None, None, None, None, None, ctypes.c_float(-1.0), 0, None) == binding.OK
+    assert lib.lite_attn_reset_mask(e.ptr, None, None) == binding.OK
+
+
+def test_status_strings():
+    for code in range(5):
+        assert tsa.lite_attn_status_string(code)
+    assert tsa.lite_attn_status_string(77) == "unknown status"
+
+
+def test_error_budget_schedule():
+    s = tsa.ErrorBudgetSchedule.linear(10, -14.0, -8.0)
+    assert s[0] == -14.0 and s[9] == -8.0 and len(s) == 10
+    tsa.ErrorBudgetSchedule([-math.inf, -12, -10, -9])
+    with pytest.raises(ValueError):
+        tsa.ErrorBudgetSchedule([-8, -10])       # tightens later
+    with pytest.raises(ValueError):
+        tsa.ErrorBudgetSchedule([0.5])
