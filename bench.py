@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the LiteAttention step on one MI355X.
+
+A step is one denoising step of the whole hot path over the workload: one lite_attn_step
+launch over every (batch, head, query tile) with the persistent skip mask, following the
+workload's error-budget schedule (a generation of T steps starts from lite_attn_reset_mask).
+Inputs for all T steps are generated on the GPU before timing and stay resident in HBM.
+
+Prints ONE JSON line:
+  value             dense-equivalent TFLOP/s over the timed steps: steps * 4*B*H*N^2*D / time
+  skipped_tile_fraction  mean fraction of tiles skipped over the timed steps
+  roofline          the attention kernel against the bf16 MFMA peak: algorithmic flops of the
+                    computed tiles per launch / mean launch duration (HIP events on the launch
+                    stream), plus HBM traffic per launch from rocprofv3 counters when they were
+                    taken on the current kernel source
+  cpu_baseline      the CPU oracle timed on this host on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dense-equiv attention TFLOP/s per denoising step; skipped-tile fraction"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 flop/clk x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3
+DEFAULT_WORKLOAD = "wan14b_720p"
+KERNEL_SOURCES = ["temporally_sparse_attention_amd/csrc/lite_attn_kernels.hip",
+                  "temporally_sparse_attention_amd/csrc/lite_attn_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: one generation)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: one generation)")
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD, help="workload name or id 1-5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
+    ap.add_argument("--per-step", action="store_true", help="add per-step times to the JSON")
+    return ap.parse_args()
+
+
+def generate(cfg, dev):
+    """Q_t, K_t for every step of the schedule and V, as bf16/fp32 [B, H, N, D] on `dev`."""
+    import torch
+    from workloads import Workload
+    wl = Workload(cfg, dev)
+    shape = (cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim)
+    qs = [torch.empty(shape, dtype=cfg.dtype, device=dev) for _ in range(cfg.steps)]
+    ks = [torch.empty(shape, dtype=cfg.dtype, device=dev) for _ in range(cfg.steps)]
+    v = torch.empty(shape, dtype=cfg.dtype, device=dev)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            for t in range(cfg.steps):
+                qt, kt, vt = wl.head_inputs(t, b, h)
+                qs[t][b, h].copy_(qt)
+                ks[t][b, h].copy_(kt)
+                if t == 0:
+                    v[b, h].copy_(vt)
+            wl._base_cache.pop((b, h), None)
+    torch.cuda.synchronize()
+    return qs, ks, v
+
+
+def computed_flops(mask, cfg, tiles_q, tiles_k):
+    """Algorithmic flops of one step given the mask at its start: 4 * rows * cols * D summed
+    over the tiles whose bit is clear (valid rows and columns only)."""
+    import torch
+    n, bq, bk = cfg.seq_len, cfg.tile_q, cfg.tile_k
+    dev = mask.device
+    j = torch.arange(tiles_k, device=dev)
+    words = mask.view(torch.int32)[..., (j // 32)]
+    bits = ((words >> (j % 32).to(torch.int32)) & 1).to(torch.float64)          # [B,H,Tq,Tk]
+    rows = torch.clamp(n - torch.arange(tiles_q, device=dev) * bq, max=bq).to(torch.float64)
+    cols = torch.clamp(n - j * bk, max=bk).to(torch.float64)
+    computed = ((1.0 - bits) * rows[:, None] * cols[None, :]).sum().item()
+    skipped_frac = bits.mean().item()
+    return 4.0 * computed * cfg.head_dim, skipped_frac
+
+
+def cpu_baseline(cfg, qs, ks, v, budget_s: float):
+    """Time the CPU oracle on whole query tiles of step 0 until `budget_s` is spent."""
+    import numpy as np
+    import torch
+    from oracle import lite_attn_step_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    bh = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    b, h = bh[int(rng.integers(len(bh)))]
+    q = qs[0][b:b + 1, h:h + 1].cpu()
+    k = ks[0][b:b + 1, h:h + 1].cpu()
+    vv = v[b:b + 1, h:h + 1].cpu()
+    tq = cfg.tiles_q
+    w = -(-cfg.tiles_k // 32)
+    mask = np.zeros((1, 1, tq, w), dtype=np.uint32)
+    order = rng.permutation(tq)
+    done, dense_flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done < len(order):
+        i = int(order[done])
+        lite_attn_step_ref(q, k, vv, mask, tile_q=cfg.tile_q, tile_k=cfg.tile_k,
+                           softmax_scale=cfg.softmax_scale, log_eps=cfg.log_eps[0], step=0,
+                           order=cfg.order, dense_prefix=cfg.dense_prefix, rows=[(0, 0, i)])
+        rows = min(cfg.tile_q, cfg.seq_len - i * cfg.tile_q)
+        dense_flops += 4.0 * rows * cfg.seq_len * cfg.head_dim
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= 2:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": dense_flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} query tiles of step 0 of {cfg.name} (batch {b}, head {h}), float64 "
+                  f"numpy oracle, {dt:.1f} s; dense-equivalent flops of those tiles / time",
+    }
+
+
+def traffic_per_launch(kernel_hash: str, workload: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counter
+    summary, if it was taken on this kernel source and workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_hash") != kernel_hash:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention of "
+              "each (batch, head) is independent and would be sharded by head across GPUs, "
+              "which this benchmark does not do.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import temporally_sparse_attention_amd as tsa
+    from workloads import get_config
+
+    cfg = get_config(args.config)
+    steps = cfg.steps if args.steps is None else args.steps
+    warmup = cfg.steps if args.warmup is None else args.warmup
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] generating {cfg.name}: B={cfg.batch} H={cfg.heads} N={cfg.seq_len} "
+        f"D={cfg.head_dim} {cfg.dtype} x {cfg.steps} steps")
+    t0 = time.perf_counter()
+    qs, ks, v = generate(cfg, dev)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    dt_name = "bf16" if cfg.dtype == torch.bfloat16 else "fp32"
+    att = tsa.LiteAttention(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, tile_q=cfg.tile_q,
+                            tile_k=cfg.tile_k, dtype=dt_name, softmax_scale=cfg.softmax_scale,
+                            order=cfg.order, dense_prefix=cfg.dense_prefix)
+    tiles_q, tiles_k = att.tiles
+    out = torch.empty_like(qs[0])
+    mask = att.new_mask(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_step(k_idx, ev=None):
+        t = k_idx % cfg.steps
+        if t == 0:
+            att.reset_mask(mask)
+        if ev is not None:
+            ev[0].record(stream)
+        att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t)
+        if ev is not None:
+            ev[1].record(stream)
+
+    # warmup
+    for k_idx in range(warmup):
+        run_step(k_idx)
+    torch.cuda.synchronize()
+
+    # timed region
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s in range(steps):
+        run_step(warmup + s, events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kernel_ms = [a.elapsed_time(b) for a, b in events]
+
+    # untimed replay of the same (deterministic) chain for per-step skipped fractions and
+    # algorithmic flops of the computed tiles
+    flops, skipped = [], []
+    mask2 = att.new_mask(dev)
+    for k_idx in range(warmup + steps):
+        t = k_idx % cfg.steps
+        if t == 0:
+            att.reset_mask(mask2)
+        if k_idx >= warmup:
+            f, sfrac = computed_flops(mask2, cfg, tiles_q, tiles_k)
+            flops.append(f)
+            skipped.append(sfrac)
+        att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
+    torch.cuda.synchronize()
+    if not torch.equal(mask, mask2):
+        log("[bench] warning: replayed mask chain differs from the timed chain")
+
+    dense = cfg.dense_flops()
+    value = steps * dense / wall / 1e12
+    mean_ms = sum(kernel_ms) / len(kernel_ms)
+    achieved = (sum(flops) / len(flops)) / (mean_ms * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if dt_name == "bf16" else FP32_PEAK_TFLOPS
+    khash = kernel_source_hash()
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic_per_launch(khash, cfg.name),
+        "kernel": f"lite_attn_fwd_{dt_name} (D={cfg.head_dim}, tile {cfg.tile_q}x{cfg.tile_k})",
+        "kernel_ms_mean": round(mean_ms, 4),
+        "flops_per_launch_mean": sum(flops) / len(flops),
+        "kernel_source_hash": khash,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu = cpu_baseline(cfg, qs, ks, v, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": cfg.batch, "heads": cfg.heads, "seq_len": cfg.seq_len,
+            "head_dim": cfg.head_dim, "tile_q": cfg.tile_q, "tile_k": cfg.tile_k,
+            "schedule_steps": cfg.steps, "softmax_scale": cfg.softmax_scale, "order": cfg.order,
+            "dense_prefix": cfg.dense_prefix, "parallelism": "single GPU",
+        },
+        "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
+        "dense_step_tflops_equiv_per_step": None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    # dense step (t = 0 of a generation) rate, if one was timed
+    dense_steps = [kernel_ms[s] for s in range(steps) if (warmup + s) % cfg.steps == 0]
+    if dense_steps:
+        result["dense_step_tflops_equiv_per_step"] = round(dense / (min(dense_steps) * 1e-3) / 1e12, 2)
+    if args.per_step:
+        result["per_step"] = [
+            {"t": (warmup + s) % cfg.steps, "kernel_ms": round(kernel_ms[s], 4),
+             "skipped": round(skipped[s], 4),
+             "computed_tflops": round(flops[s] / (kernel_ms[s] * 1e-3) / 1e12, 2)}
+            for s in range(steps)]
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
