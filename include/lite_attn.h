@@ -76,7 +76,7 @@ typedef struct lite_attn_config {
                             or columns touch them is never flagged. 0 = off; <= seq_len */
   int64_t stride_b;      /* element strides shared by q, k, v, out; all three zero selects */
   int64_t stride_h;      /* the contiguous layout [B][H][N][D]. Each must be a multiple of */
-  int64_t stride_n;      /* 8 elements (16 bytes) so that rows stay 16-byte aligned.       */
+  int64_t stride_n;      /* 8 elements (16 bytes); head_dim <= stride_n < 2^24.            */
 } lite_attn_config;
 
 typedef struct lite_attn_s* lite_attn_t;
@@ -85,7 +85,7 @@ typedef struct lite_attn_s* lite_attn_t;
  * LiteAttention, page 1 "Architecture Overview": the Skip-Mask bitmask and QK-Skip.
  * Returns INVALID_ARG for NULL arguments, a wrong abi_version, negative sizes, strides that
  * are not multiples of 8 elements, or dense_prefix outside [0, seq_len]; UNSUPPORTED for a
- * head_dim / tile / dtype combination without a kernel or for Tk > 4096 (N > 262144 with
+ * head_dim / tile / dtype combination without a kernel or for Tk > 2048 (N > 131072 with
  * 64-key tiles). On failure *out is set to NULL. */
 int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out);
 

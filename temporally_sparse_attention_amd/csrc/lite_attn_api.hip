@@ -85,10 +85,10 @@ int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
       sh = (int64_t)c.seq_len * sn;
       sb = (int64_t)c.heads * sh;
     }
-    if (sb < 0 || sh < 0 || sn < c.head_dim || sb % 8 || sh % 8 || sn % 8)
+    if (sb < 0 || sh < 0 || sn < c.head_dim || sb % 8 || sh % 8 || sn % 8 || sn >= (1 << 24))
       return fail(LITE_ATTN_ERR_INVALID_ARG,
                   "create: strides (%lld, %lld, %lld) must be non-negative multiples of 8 "
-                  "elements with stride_n >= head_dim",
+                  "elements with head_dim <= stride_n < 2^24",
                   (long long)sb, (long long)sh, (long long)sn);
 
     if (c.tile_k != lite_attn::kTileK)

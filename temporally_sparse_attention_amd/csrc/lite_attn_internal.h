@@ -7,7 +7,7 @@
 namespace lite_attn {
 
 constexpr int kTileK = 64;          // keys per tile (two 32-key MFMA blocks)
-constexpr int kMaxTilesK = 4096;    // visiting list capacity per query tile (LDS)
+constexpr int kMaxTilesK = 2048;    // visiting list capacity per query tile (LDS)
 constexpr int kMaxWords = kMaxTilesK / 32;
 
 // Everything one forward launch needs. Strides are in elements.

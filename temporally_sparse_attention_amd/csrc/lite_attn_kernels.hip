@@ -38,6 +38,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -135,42 +136,63 @@ __device__ void write_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* ke
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 kernel: MFMA 32x32x16 bf16, K/V double-buffered in LDS, one barrier per tile.
+// bf16 kernel: MFMA 32x32x16 bf16; K/V streamed straight into LDS (double-buffered) with
+// buffer loads; one workgroup barrier per visited key tile.
 // ---------------------------------------------------------------------------------------
 
-// LDS layouts (bf16 elements):
-//  K tile  [64 keys][D]: 16-byte chunk c of key row r is stored at chunk c ^ (r & 7), which
-//          makes both the coalesced row-wise writes and the 32-rows-one-column operand reads
-//          bank-conflict free.
-//  V^T tile [D][64 keys]: row d holds the 64 keys of feature d. Within each 16-key group the
-//          keys are stored in MFMA operand order (bits 2 and 3 of the key index swapped), so a
-//          lane's 8 operand keys are one 16-byte chunk; chunk c of row d is stored at
-//          c ^ ((d ^ (d >> 3)) & 7), which spreads both the transposing 8-byte writes and the
-//          16-byte operand reads over all banks.
-__device__ __forceinline__ int k_lds_off(int row, int chunk, int D) {
-  return row * D + ((chunk ^ (row & 7)) << 3);
+// LDS layouts (bf16, row-major [64 keys][D] for both tiles, rows padded):
+//  K rows are D*2 + 16 bytes apart. The S^T operand read has lanes 0..31 reading one 16-byte
+//  column chunk of 32 consecutive rows; the 16-byte row skew puts every 8 consecutive rows on
+//  distinct banks.
+//  V rows are D*2 + 32 bytes apart. The V^T operand is read with ds_read_b64_tr_b16: each
+//  16-lane group reads 4 consecutive rows x 32 bytes and receives them transposed (lane i gets
+//  column i of the 4 rows). The 32-byte row skew puts those 4 row segments on distinct banks.
+//  Both layouts keep every operand address a per-lane base plus a compile-time offset.
+//  The tiles are written by buffer_load_dwordx4 ... lds: each instruction deposits 64 lanes x
+//  16 bytes contiguously, so the k-th 16-byte slot of a tile is filled by the lane whose
+//  source address is the matching (row, chunk) of global memory; padding slots read an
+//  out-of-range offset and receive zeros without touching memory. Keys >= N are outside the
+//  buffer's range and read as zeros too.
+template <int D>
+struct Bf16TileGeom {
+  static constexpr int CH = D / 8;           // 16-byte chunks of one K or V row
+  static constexpr int KCH = CH + 1;         // padded K row, in chunks
+  static constexpr int VCH = CH + 2;         // padded V row, in chunks
+  static constexpr int K_BYTES = BK * KCH * 16;
+  static constexpr int V_BYTES = BK * VCH * 16;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond every buffer range used here
+
+// Device-only helpers and kernel bodies below use AMDGPU buffer-resource types that the host
+// compilation pass cannot represent; the host pass only needs the kernels' launch stubs.
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+#endif
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = Bf16TileGeom<D>;
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
-  constexpr int KCH = D / 8;                          // 16-byte chunks per K row
-  constexpr int KLD = (BK * KCH) / NT;                // K chunks per thread per tile
-  constexpr int VUNITS = (BK / 4) * (D / 8);          // (4 keys x 8 features) units per tile
-  constexpr int VLD = (VUNITS + NT - 1) / NT;         // units per thread per tile
-  static_assert((BK * KCH) % NT == 0, "K tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_k[2][BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 s_vt[2][D * BK];
+  __shared__ __attribute__((aligned(16))) unsigned char s_kv[2 * G::STAGE_BYTES];
   __shared__ uint16_t s_list[kMaxTilesK];
   __shared__ uint32_t s_keep[kMaxWords];
   __shared__ int s_count;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -186,6 +208,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   uint32_t* mrow = p.mask + (size_t)tile * p.W;
   const int N = p.N;
   const int64_t sn = p.sn;
+  const uint32_t row_bytes = (uint32_t)sn * 2u;
 
   const int cnt = build_visit_list<NT>(mrow, p.W, p.Tk, p.descending != 0, s_list, s_keep,
                                        &s_count);
@@ -204,82 +227,74 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     }
   }
 
-  // ---- K/V pipeline: global -> registers (prefetch) -> LDS ----
-  u32x4 kreg[KLD];
-  u32x4 vreg[VLD][4];
-  auto load_kv = [&](int j) {
+  // Per-lane source offsets of this wave's share of the tile loads (loop invariant).
+  // Load instruction x (64 lanes) fills the 16-byte slots [64x, 64x + 64) of a tile; the
+  // instructions are dealt round-robin to the waves.
+  constexpr int KLOADS = (G::KCH + NW - 1) / NW;
+  constexpr int VLOADS = (G::VCH + NW - 1) / NW;
+  uint32_t koff[KLOADS], voff[VLOADS];
+#pragma unroll
+  for (int n = 0; n < KLOADS; ++n) {
+    const int slot = 64 * (wave + NW * n) + lane;
+    const int row = slot / G::KCH, ch = slot % G::KCH;
+    koff[n] = ch < G::CH ? (uint32_t)row * row_bytes + 16u * ch : kOobOffset;
+  }
+#pragma unroll
+  for (int n = 0; n < VLOADS; ++n) {
+    const int slot = 64 * (wave + NW * n) + lane;
+    const int row = slot / G::VCH, ch = slot % G::VCH;
+    voff[n] = ch < G::CH ? (uint32_t)row * row_bytes + 16u * ch : kOobOffset;
+  }
+
+  auto issue_tile_loads = [&](int j, int buf) {
     const int key0 = j * BK;
+    const int rows = min(BK, N - key0);
+    const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (int64_t)key0 * sn, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (int64_t)key0 * sn, bytes);
+    unsigned char* stage = s_kv + buf * G::STAGE_BYTES;
 #pragma unroll
-    for (int x = 0; x < KLD; ++x) {
-      const int ch = tid + NT * x;
-      const int row = ch / KCH, cc = ch % KCH;
-      const int key = key0 + row;
-      kreg[x] = key < N ? *reinterpret_cast<const u32x4*>(kh + (int64_t)key * sn + cc * 8)
-                        : u32x4{0u, 0u, 0u, 0u};
+    for (int n = 0; n < KLOADS; ++n) {
+      const int x = wave + NW * n;
+      if (KLOADS * NW == G::KCH || x < G::KCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + x * 1024), 16, koff[n],
+                                                 0, 0, 0);
     }
 #pragma unroll
-    for (int x = 0; x < VLD; ++x) {
-      const int u = tid + NT * x;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int kg = u / (D / 8), dg = u % (D / 8);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int key = key0 + 4 * kg + kk;
-          vreg[x][kk] = key < N ? *reinterpret_cast<const u32x4*>(vh + (int64_t)key * sn + dg * 8)
-                                : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < KLD; ++x) {
-      const int ch = tid + NT * x;
-      const int row = ch / KCH, cc = ch % KCH;
-      *reinterpret_cast<u32x4*>(&s_k[buf][k_lds_off(row, cc, D)]) = kreg[x];
-    }
-#pragma unroll
-    for (int x = 0; x < VLD; ++x) {
-      const int u = tid + NT * x;
-      if (VUNITS % NT == 0 || u < VUNITS) {
-        const int kg = u / (D / 8), dg = u % (D / 8);
-        const int g4 = kg & 3;                       // 4-key group inside a 16-key group
-        const int pos = 16 * (kg >> 2) + 8 * (g4 & 1) + 4 * (g4 >> 1);  // operand order
-        const int lc = pos >> 3, hf = (pos >> 2) & 1;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int sh = 16 * (m & 1);
-          const uint32_t e0 = (vreg[x][0][m >> 1] >> sh) & 0xffffu;
-          const uint32_t e1 = (vreg[x][1][m >> 1] >> sh) & 0xffffu;
-          const uint32_t e2 = (vreg[x][2][m >> 1] >> sh) & 0xffffu;
-          const uint32_t e3 = (vreg[x][3][m >> 1] >> sh) & 0xffffu;
-          const int d = 8 * dg + m;
-          const int off = d * BK + ((lc ^ vt_swz(d)) << 3) + 4 * hf;
-          *reinterpret_cast<u32x2*>(&s_vt[buf][off]) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-        }
-      }
+    for (int n = 0; n < VLOADS; ++n) {
+      const int x = wave + NW * n;
+      if (VLOADS * NW == G::VCH || x < G::VCH)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + G::K_BYTES + x * 1024),
+                                                 16, voff[n], 0, 0, 0);
     }
   };
 
-  float m_run = -INFINITY;   // running row maximum (raw scores)
+  // Per-lane LDS read bases (bytes within a stage).
+  // K operand for key block kb, feature step c: row 32kb + l32, chunk 2c + half.
+  const int k_rd = l32 * (G::KCH * 16) + half * 16;
+  // V^T operand for feature block db, 16-key step kc: two transposed 4-row reads at rows
+  // 16kc + 4*half (+8), columns 32db + 16*(group & 1) + 4*(lane & 3) of each 16-lane group.
+  const int grp = lane >> 4, gi = lane & 15;
+  const int v_rd = G::K_BYTES + (4 * half + (gi >> 2)) * (G::VCH * 16) +
+                   2 * (16 * (grp & 1) + 4 * (gi & 3));
+
+  float m_run = -INFINITY;   // running row maximum of raw scores (the QK-Skip reference)
+  float m_ref = -INFINITY;   // exponent reference of the accumulators (lags m_run by < 2^8)
   float l_run = 0.f;         // this lane's partial row sum (its 32 keys of every tile)
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
   const float c2 = p.scale_log2;
-  if (cnt > 0) {
-    load_kv(s_list[0]);
-    store_kv(0);
-    if (cnt > 1) load_kv(s_list[1]);
-    __syncthreads();
-  }
+  if (cnt > 0) issue_tile_loads(s_list[0], 0);
 
   for (int n = 0; n < cnt; ++n) {
-    const int j = s_list[n];
+    const int j = __builtin_amdgcn_readfirstlane(s_list[n]);
     const int buf = n & 1;
-    if (n + 1 < cnt) store_kv(buf ^ 1);
-    if (n + 2 < cnt) load_kv(s_list[n + 2]);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile n landed
+    __syncthreads();                                      // everyone's landed; tile n-1 consumed
+    if (n + 1 < cnt) issue_tile_loads(__builtin_amdgcn_readfirstlane(s_list[n + 1]), buf ^ 1);
+    const unsigned char* stage = s_kv + buf * G::STAGE_BYTES;
 
     // S^T = K Q^T for keys [32kb, 32kb+32) of the tile: lane holds query l32 and keys
     // 32kb + 8(r/4) + 4*half + (r%4) in register r.
@@ -287,11 +302,10 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const int row = 32 * kb + l32;
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&s_k[buf][k_lds_off(row, 2 * c + half, D)]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            stage + k_rd + kb * 32 * (G::KCH * 16) + c * 32);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
       }
     }
@@ -315,52 +329,67 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
     mt = halves_max(mt);
 
-    // QK-Skip vote: keep the tile if any valid row's local max is not far enough below the
-    // running max (a NaN difference keeps it too).
+    // QK-Skip vote against the running maximum of the tiles visited before this one.
     const float diff = (mt - m_run) * p.scale;
     const bool below = !row_valid || (diff < p.log_eps);
     if (__ballot(!below) != 0ull) {
       if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
     }
+    m_run = fmaxf(m_run, mt);
 
-    // Online softmax update (base 2: exp(x*scale) = exp2(x*scale*log2 e)).
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-    const float nb = -m_new * c2;
-    float psum = 0.f;
+    // Lazy rescale: move the exponent reference only when some row's maximum exceeds it by
+    // more than 2^8 in exp2 units, so exponentials stay <= 256 and the common case skips the
+    // accumulator rescale entirely.
+    if (__ballot((m_run - m_ref) * c2 > 8.f) != 0ull) {
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
+      m_ref = m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+    const float nb = -m_ref * c2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, nb));
-        s[kb][r] = e;
-        psum += e;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, nb));
 
-    // P as bf16 B operands: 16-key step kc uses registers 8(kc%2) .. +7 of s[kc/2].
+    // P as bf16 B operands: 16-key step kc uses registers 8(kc%2) .. +7 of s[kc/2], i.e. keys
+    // 16kc + 4*half + {0..3} and 16kc + 8 + 4*half + {0..3}. The row sum is taken over the same
+    // bf16-rounded weights the PV product consumes (v_dot2 against a pair of ones), so that
+    // numerator and denominator of the softmax agree.
     bf16x8 pb[4];
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) pb[kc][m] = (__bf16)s[kc >> 1][8 * (kc & 1) + m];
+#pragma unroll
+      for (int m = 0; m < 8; m += 2) {
+        const bf16x2 pr = {pb[kc][m], pb[kc][m + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+      }
+    }
+    l_run += psum;
 
     // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4).
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int d = 32 * db + l32;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &s_vt[buf][d * BK + (((2 * kc + half) ^ vt_swz(d)) << 3)]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], o[db], 0, 0, 0);
+        const unsigned char* base = stage + v_rd + kc * 16 * (G::VCH * 16) + db * 64;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)(base + 8 * (G::VCH * 16)));
+        bf16x8 av;
+        const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
+        av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
+        av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc], o[db], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // Epilogue: normalise and store this wave's rows.
   const float l_tot = halves_sum(l_run);
@@ -380,6 +409,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
 
   const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
   write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, i * BQ < p.dense_prefix, exempt_cols);
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------

@@ -80,7 +80,7 @@ def test_create_validation():
     assert _status(ok(dense_prefix=-1)) == binding.ERR_INVALID_ARG
     assert _status(ok(strides=(0, 0, 100))) == binding.ERR_INVALID_ARG     # not a multiple of 8
     assert _status(ok(strides=(0, 0, 64))) == binding.ERR_INVALID_ARG      # < head_dim
-    assert _status(lambda: tsa.lite_attn_create(1, 1, 300000, 64, tile_q=128)) == binding.ERR_UNSUPPORTED
+    assert _status(lambda: tsa.lite_attn_create(1, 1, 140000, 64, tile_q=128)) == binding.ERR_UNSUPPORTED
     cfg = tsa.make_config(1, 2, 1000, 128)
     cfg.abi_version = 99
     assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=cfg)) == binding.ERR_INVALID_ARG
