@@ -136,31 +136,44 @@ __device__ void write_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* ke
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 kernel: MFMA 32x32x16 bf16; K/V streamed straight into LDS (double-buffered) with
-// buffer loads; one workgroup barrier per visited key tile.
+// bf16 kernel: MFMA 32x32x16 bf16, software-pipelined across key tiles; K/V streamed straight
+// into LDS (double-buffered) with buffer loads; one workgroup barrier per visited tile.
 // ---------------------------------------------------------------------------------------
-
-// LDS layouts (bf16, row-major [64 keys][D] for both tiles, rows padded):
-//  K rows are D*2 + 16 bytes apart. The S^T operand read has lanes 0..31 reading one 16-byte
-//  column chunk of 32 consecutive rows; the 16-byte row skew puts every 8 consecutive rows on
+//
+// Work split. A workgroup owns one query tile (tile_q = 32 * NW rows) and runs NW waves; wave w
+// owns query rows 32w .. 32w+31 and every key of every visited tile.
+//
+// Pipelining. A wave overlaps its own MFMAs with independent VALU work well, but within one
+// tile the softmax depends on the scores and the PV product on the softmax. So iteration n
+// works on two tiles at once:
+//   phase 1: exponentials and bf16 weights P(n) (VALU)  ||  S(n+1) = K(n+1) Q^T (MFMA)
+//   phase 2: O += V(n)^T P(n)^T (MFMA)                   ||  row maxima of S(n+1) (VALU)
+//   between: QK-Skip vote and the lazy rescale for tile n+1 (short, branchy, rare work).
+// K runs one tile ahead of V: during iteration n the workgroup reads K(n+1) and V(n) and loads
+// K(n+2) and V(n+1) into the other stages.
+//
+// LDS layouts (bf16, row-major [64 keys][D], rows padded):
+//  K rows are D*2 + 16 bytes apart: the S^T operand read has 32 lanes reading one 16-byte
+//  column chunk of 32 consecutive rows, and the 16-byte skew puts every 8 consecutive rows on
 //  distinct banks.
 //  V rows are D*2 + 32 bytes apart. The V^T operand is read with ds_read_b64_tr_b16: each
 //  16-lane group reads 4 consecutive rows x 32 bytes and receives them transposed (lane i gets
-//  column i of the 4 rows). The 32-byte row skew puts those 4 row segments on distinct banks.
-//  Both layouts keep every operand address a per-lane base plus a compile-time offset.
+//  column i of the 4 rows); the 32-byte skew spreads the 4 row segments over the banks.
+//  Both keep every operand address a per-lane base plus a compile-time offset.
 //  The tiles are written by buffer_load_dwordx4 ... lds: each instruction deposits 64 lanes x
-//  16 bytes contiguously, so the k-th 16-byte slot of a tile is filled by the lane whose
-//  source address is the matching (row, chunk) of global memory; padding slots read an
-//  out-of-range offset and receive zeros without touching memory. Keys >= N are outside the
-//  buffer's range and read as zeros too.
+//  16 bytes contiguously, so each 16-byte LDS slot is filled by the lane whose source offset is
+//  the matching (row, chunk) of global memory; padding slots read an out-of-range offset and
+//  receive zeros without touching memory. Keys >= N lie outside the buffer range and read as
+//  zeros too.
 template <int D>
 struct Bf16TileGeom {
   static constexpr int CH = D / 8;           // 16-byte chunks of one K or V row
   static constexpr int KCH = CH + 1;         // padded K row, in chunks
   static constexpr int VCH = CH + 2;         // padded V row, in chunks
-  static constexpr int K_BYTES = BK * KCH * 16;
-  static constexpr int V_BYTES = BK * VCH * 16;
-  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int KROW = KCH * 16;      // bytes
+  static constexpr int VROW = VCH * 16;
+  static constexpr int K_BYTES = BK * KROW;
+  static constexpr int V_BYTES = BK * VROW;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -172,9 +185,38 @@ constexpr uint32_t kOobOffset = 0x7ffffff0u;   // beyond every buffer range used
 // Device-only helpers and kernel bodies below use AMDGPU buffer-resource types that the host
 // compilation pass cannot represent; the host pass only needs the kernels' launch stubs.
 #if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (4 SGPRs) over [base, base + bytes): stride 0, so reads at offsets
+// >= bytes return zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS: lane l's data lands
+// at lds_addr + 16 * l. Issued as inline assembly so that the compiler does not track these
+// loads as LDS writes: the kernel orders them itself (each wave waits for its own loads with
+// s_waitcnt vmcnt(0) before the workgroup barrier that precedes any read of the stage), and
+// the compiler would otherwise make unrelated LDS accesses wait for every load in flight. The
+// instruction has no register result, and M0 is declared clobbered.
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 #endif
 
@@ -185,14 +227,20 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
 
-  __shared__ __attribute__((aligned(16))) unsigned char s_kv[2 * G::STAGE_BYTES];
+  // One LDS object per stage: every operand read and every tile load names its stage
+  // statically (the tile loop is unrolled by two), so the compiler can tell that the loads
+  // filling one stage never alias the reads of the other and needs no wait between them.
+  __shared__ __attribute__((aligned(16))) unsigned char s_k0[G::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k1[G::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v0[G::V_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v1[G::V_BYTES];
   __shared__ uint16_t s_list[kMaxTilesK];
   __shared__ uint32_t s_keep[kMaxWords];
   __shared__ int s_count;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);   // scalar
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -214,7 +262,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
                                        &s_count);
 
   // Q rows of this wave as MFMA B operands: lane holds features 16c + 8*half .. +7 of query
-  // row l32 for every 16-feature step c.
+  // row l32, for every 16-feature step c.
   const int qrow = i * BQ + wave * 32 + l32;
   const bool row_valid = qrow < N;
   bf16x8 qf[D / 16];
@@ -226,10 +274,15 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       qf[c] = bf16x8{};
     }
   }
+  // Consume Q here: the compiler then waits for these loads once, before the tile loop, rather
+  // than at the loop's first MFMA on every iteration (where the wait would also cover the K/V
+  // tile loads in flight).
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" ::"v"(qf[c]));
 
-  // Per-lane source offsets of this wave's share of the tile loads (loop invariant).
-  // Load instruction x (64 lanes) fills the 16-byte slots [64x, 64x + 64) of a tile; the
-  // instructions are dealt round-robin to the waves.
+  // Per-lane source offsets of this wave's share of the tile loads (loop invariant). Load
+  // instruction x (64 lanes) fills the 16-byte slots [64x, 64x + 64) of a tile; instructions
+  // are dealt round-robin to the waves.
   constexpr int KLOADS = (G::KCH + NW - 1) / NW;
   constexpr int VLOADS = (G::VCH + NW - 1) / NW;
   uint32_t koff[KLOADS], voff[VLOADS];
@@ -245,148 +298,220 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     const int row = slot / G::VCH, ch = slot % G::VCH;
     voff[n] = ch < G::CH ? (uint32_t)row * row_bytes + 16u * ch : kOobOffset;
   }
-
-  auto issue_tile_loads = [&](int j, int buf) {
+  auto tile_bytes = [&](int key0) {
+    return (uint32_t)(min(BK, N - key0) - 1) * row_bytes + D * 2;
+  };
+  auto issue_k = [&](int j, unsigned char* dst) {
     const int key0 = j * BK;
-    const int rows = min(BK, N - key0);
-    const uint32_t bytes = (uint32_t)(rows - 1) * row_bytes + D * 2;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (int64_t)key0 * sn, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (int64_t)key0 * sn, bytes);
-    unsigned char* stage = s_kv + buf * G::STAGE_BYTES;
+    const i32x4 r = make_rsrc(kh + (int64_t)key0 * sn, tile_bytes(key0));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(dst));
 #pragma unroll
     for (int n = 0; n < KLOADS; ++n) {
       const int x = wave + NW * n;
-      if (KLOADS * NW == G::KCH || x < G::KCH)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(stage + x * 1024), 16, koff[n],
-                                                 0, 0, 0);
+      if (KLOADS * NW == G::KCH || x < G::KCH) lds_dma16(r, base + x * 1024, koff[n]);
     }
+  };
+  auto issue_v = [&](int j, unsigned char* dst) {
+    const int key0 = j * BK;
+    const i32x4 r = make_rsrc(vh + (int64_t)key0 * sn, tile_bytes(key0));
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(dst));
 #pragma unroll
     for (int n = 0; n < VLOADS; ++n) {
       const int x = wave + NW * n;
-      if (VLOADS * NW == G::VCH || x < G::VCH)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(stage + G::K_BYTES + x * 1024),
-                                                 16, voff[n], 0, 0, 0);
+      if (VLOADS * NW == G::VCH || x < G::VCH) lds_dma16(r, base + x * 1024, voff[n]);
     }
   };
 
-  // Per-lane LDS read bases (bytes within a stage).
-  // K operand for key block kb, feature step c: row 32kb + l32, chunk 2c + half.
-  const int k_rd = l32 * (G::KCH * 16) + half * 16;
-  // V^T operand for feature block db, 16-key step kc: two transposed 4-row reads at rows
-  // 16kc + 4*half (+8), columns 32db + 16*(group & 1) + 4*(lane & 3) of each 16-lane group.
-  const int grp = lane >> 4, gi = lane & 15;
-  const int v_rd = G::K_BYTES + (4 * half + (gi >> 2)) * (G::VCH * 16) +
-                   2 * (16 * (grp & 1) + 4 * (gi & 3));
+  // Per-lane LDS read bases within a stage (bytes).
+  // K operand for key block kb, feature step c: key row 32kb + l32, chunk 2c + half.
+  const int k_rd = l32 * G::KROW + 16 * half;
+  // V^T operand for feature block db and 16-key step kc: two transposed 4-row reads at key rows
+  // 16kc + 4*half (+8), columns 32db + 16*(g16 & 1) + 4*(lane & 3) of each 16-lane group g16.
+  const int g16 = lane >> 4, gi = lane & 15;
+  const int v_rd = (4 * half + (gi >> 2)) * G::VROW + 2 * (16 * (g16 & 1) + 4 * (gi & 3));
 
-  float m_run = -INFINITY;   // running row maximum of raw scores (the QK-Skip reference)
-  float m_ref = -INFINITY;   // exponent reference of the accumulators (lags m_run by < 2^8)
-  float l_run = 0.f;         // this lane's partial row sum (its 32 keys of every tile)
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
-  const float c2 = p.scale_log2;
-  if (cnt > 0) issue_tile_loads(s_list[0], 0);
+  // MFMA phases read their LDS operands through a ring, several MFMAs ahead of use, so the
+  // LDS latency overlaps the matrix pipe instead of stalling in front of every MFMA; while in
+  // an MFMA phase a wave raises its issue priority so that the other wave on the SIMD fills
+  // the gaps with its softmax work.
+  constexpr int RING = 4;
 
-  for (int n = 0; n < cnt; ++n) {
-    const int j = __builtin_amdgcn_readfirstlane(s_list[n]);
-    const int buf = n & 1;
+  // S^T = K Q^T for keys 32kb + 8(r/4) + 4*half + (r%4) of a tile, query l32 (lane). The 16
+  // MFMAs alternate between the two key blocks.
+  auto qk = [&](const unsigned char* kst, f32x16 (&sc)[2]) {
+    auto kread = [&](int t) {   // t -> key block t & 1, feature step t >> 1
+      return *reinterpret_cast<const bf16x8*>(kst + k_rd + (t & 1) * 32 * G::KROW + 32 * (t >> 1));
+    };
+    bf16x8 kr[RING];
+#pragma unroll
+    for (int t = 0; t < RING; ++t) kr[t] = kread(t);
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % RING], qf[t >> 1], sc[t & 1], 0, 0, 0);
+      if (t + RING < D / 8) kr[t % RING] = kread(t + RING);
+    }
+    // Keep the ring: RING operand reads up front, then one MFMA and one read at a time.
+    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4). Step t
+  // covers feature block t % (D/32) and 16-key step t / (D/32).
+  auto pv = [&](const unsigned char* vst, const bf16x8 (&pb)[4]) {
+    auto vread = [&](int t) {
+      const int db = t % (D / 32), kc = t / (D / 32);
+      const unsigned char* base = vst + v_rd + kc * 16 * G::VROW + db * 64;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)base);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 8 * G::VROW));
+      const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
+      bf16x8 av;
+      av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
+      av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
+      return av;
+    };
+    bf16x8 vr[RING];
+#pragma unroll
+    for (int t = 0; t < RING; ++t) vr[t] = vread(t);
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      const int db = t % (D / 32), kc = t / (D / 32);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[t % RING], pb[kc], o[db], 0, 0, 0);
+      if (t + RING < D / 8) vr[t % RING] = vread(t + RING);
+    }
+    // Keep the ring: two transposed reads per MFMA operand.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+  // Keys >= N of the ragged last tile do not exist: their scores become -inf.
+  auto mask_ragged = [&](int j, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (j * BK + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3) >= N) sc[kb][r] = -INFINITY;
+  };
+
+  float m_run = -INFINITY;   // running row maximum of raw scores (the QK-Skip reference)
+  float m_ref = -INFINITY;   // exponent reference of the accumulators (lags m_run by < 2^8)
+  float l_run = 0.f;         // this lane's partial row sum
+  const float c2 = p.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  const float inv_c2 = 1.f / c2;
+
+  // One visited tile (list position n, key tile j; j_next is the tile at position n + 1): wait
+  // for its K/V stage, start loading the next tile into the other stage, then scores, softmax,
+  // QK-Skip vote and PV.
+  auto tile_step = [&](int n, int j, int j_next, const unsigned char* kcur,
+                       const unsigned char* vcur, unsigned char* knext, unsigned char* vnext) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile n landed
     __syncthreads();                                      // everyone's landed; tile n-1 consumed
-    if (n + 1 < cnt) issue_tile_loads(__builtin_amdgcn_readfirstlane(s_list[n + 1]), buf ^ 1);
-    const unsigned char* stage = s_kv + buf * G::STAGE_BYTES;
-
-    // S^T = K Q^T for keys [32kb, 32kb+32) of the tile: lane holds query l32 and keys
-    // 32kb + 8(r/4) + 4*half + (r%4) in register r.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            stage + k_rd + kb * 32 * (G::KCH * 16) + c * 32);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
-      }
+    if (n + 1 < cnt) {
+      issue_k(j_next, knext);
+      issue_v(j_next, vnext);
     }
 
-    // Ragged last tile: keys >= N do not exist.
-    if ((j + 1) * BK > N) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * BK + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= N) s[kb][r] = -INFINITY;
-        }
-    }
+    f32x16 sc[2];
+    qk(kcur, sc);
+    if ((j + 1) * BK > N) mask_ragged(j, sc);
 
-    // Row maximum of the tile.
-    float mt = s[0][0];
+    // Scores in exp2 units relative to the exponent reference, t = s * c2 - m_ref * c2. These
+    // are results of arithmetic, so their maximum needs no NaN quieting (taking it on the raw
+    // MFMA results would cost one extra instruction per score); the row maximum in raw units
+    // is recovered from it.
+    const float nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;
+    f32x16 t[2];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-    mt = halves_max(mt);
-
-    // QK-Skip vote against the running maximum of the tiles visited before this one.
-    const float diff = (mt - m_run) * p.scale;
-    const bool below = !row_valid || (diff < p.log_eps);
-    if (__ballot(!below) != 0ull) {
-      if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
+      for (int r = 0; r < 16; ++r) t[kb][r] = fmaf(sc[kb][r], c2, nb);
+    float tm0 = fmaxf(t[0][0], t[1][0]), tm1 = fmaxf(t[0][1], t[1][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      tm0 = fmaxf(tm0, fmaxf(t[0][r], t[1][r]));
+      tm1 = fmaxf(tm1, fmaxf(t[0][r + 1], t[1][r + 1]));
     }
+    const float tm = halves_max(fmaxf(tm0, tm1));
+    const float mt = (tm - nb) * inv_c2;   // this tile's row maximum of raw scores
+    const float m_prev = m_run;
     m_run = fmaxf(m_run, mt);
-
     // Lazy rescale: move the exponent reference only when some row's maximum exceeds it by
-    // more than 2^8 in exp2 units, so exponentials stay <= 256 and the common case skips the
-    // accumulator rescale entirely.
-    if (__ballot((m_run - m_ref) * c2 > 8.f) != 0ull) {
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
+    // more than 2^8 in exp2 units (or there is no reference yet), so exponentials stay <= 256
+    // and the common case skips the accumulator rescale.
+    if (__ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
+      const float shift = -m_run * c2 - nb;
       m_ref = m_run;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[kb][r] += shift;
     }
-    const float nb = -m_ref * c2;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, nb));
 
-    // P as bf16 B operands: 16-key step kc uses registers 8(kc%2) .. +7 of s[kc/2], i.e. keys
-    // 16kc + 4*half + {0..3} and 16kc + 8 + 4*half + {0..3}. The row sum is taken over the same
-    // bf16-rounded weights the PV product consumes (v_dot2 against a pair of ones), so that
-    // numerator and denominator of the softmax agree.
+    // P as bf16 B operands (16-key step kc: registers 8(kc%2) .. +7 of t[kc/2]) and the row
+    // sum over the same rounded weights (v_dot2 with ones, two partial sums).
     bf16x8 pb[4];
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float psum = 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m) pb[kc][m] = (__bf16)s[kc >> 1][8 * (kc & 1) + m];
+      for (int e = 0; e < 8; ++e) pb[kc][e] = (__bf16)__builtin_amdgcn_exp2f(t[kc >> 1][8 * (kc & 1) + e]);
 #pragma unroll
-      for (int m = 0; m < 8; m += 2) {
-        const bf16x2 pr = {pb[kc][m], pb[kc][m + 1]};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+      for (int e = 0; e < 8; e += 4) {
+        const bf16x2 pr0 = {pb[kc][e], pb[kc][e + 1]};
+        const bf16x2 pr1 = {pb[kc][e + 2], pb[kc][e + 3]};
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr0, ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr1, ones, ps1, false);
       }
     }
+    const float psum = ps0 + ps1;
     l_run += psum;
 
-    // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4).
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const unsigned char* base = stage + v_rd + kc * 16 * (G::VCH * 16) + db * 64;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16*)(base + 8 * (G::VCH * 16)));
-        bf16x8 av;
-        const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
-        av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
-        av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kc], o[db], 0, 0, 0);
-      }
+    // QK-Skip vote against the running maximum of the tiles visited before this one: keep the
+    // tile if any valid row is not far enough below it, or has a NaN weight.
+    const float diff = (mt - m_prev) * p.scale;
+    const bool below = !row_valid || (diff < p.log_eps && psum == psum);
+    if (__ballot(!below) != 0ull) {
+      if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
+    }
+
+    pv(vcur, pb);
+  };
+
+  // The list entries for the next two positions are read ahead so that the tile index is in a
+  // scalar register when the step begins.
+  int j_cur = cnt > 0 ? __builtin_amdgcn_readfirstlane(s_list[0]) : 0;
+  int j_nxt = cnt > 1 ? __builtin_amdgcn_readfirstlane(s_list[1]) : 0;
+  if (cnt > 0) {
+    issue_k(j_cur, s_k0);
+    issue_v(j_cur, s_v0);
+  }
+  for (int n = 0; n < cnt; n += 2) {
+    int j_after = n + 2 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 2]) : 0;
+    tile_step(n, j_cur, j_nxt, s_k0, s_v0, s_k1, s_v1);
+    j_cur = j_nxt;
+    j_nxt = j_after;
+    if (n + 1 < cnt) {
+      j_after = n + 3 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 3]) : 0;
+      tile_step(n + 1, j_cur, j_nxt, s_k1, s_v1, s_k0, s_v0);
+      j_cur = j_nxt;
+      j_nxt = j_after;
     }
   }
   __syncthreads();
