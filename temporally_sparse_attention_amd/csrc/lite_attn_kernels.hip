@@ -41,6 +41,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -60,14 +61,6 @@ __device__ __forceinline__ uint32_t valid_bits(int w, int Tk) {
 __device__ __forceinline__ uint32_t low_bits(int w, int jp) {
   const int rem = jp - 32 * w;
   return rem >= 32 ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
-}
-
-// Workgroups are dispatched to the 8 XCDs round-robin by block index. Remap so that each
-// XCD receives a contiguous range of logical tiles: consecutive query tiles of one head then
-// run on the same XCD and share its L2 for the K/V stream.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
-  const uint32_t per = n / 8u, rem = n % 8u, xcd = bid % 8u, loc = bid / 8u;
-  return xcd < rem ? xcd * (per + 1u) + loc : rem * (per + 1u) + (xcd - rem) * per + loc;
 }
 
 // Value of x in the other half-wave (lane ^ 32) combined with x by max / sum.
@@ -244,7 +237,11 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);  // = (b * H + h) * Tq + i
+  // Block index = logical tile (b * H + h) * Tq + i. Workgroups are dispatched to the 8 XCDs
+  // round-robin, so each XCD receives every 8th query tile of every head: an even share of
+  // every head and of every region of a head, which keeps the XCDs balanced when skip
+  // densities differ, while all XCDs stream the same head's K/V (it stays in the MALL).
+  const uint32_t tile = blockIdx.x;
   const int i = (int)(tile % (uint32_t)p.Tq);
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
@@ -470,15 +467,17 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
+      u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[kc][e] = (__bf16)__builtin_amdgcn_exp2f(t[kc >> 1][8 * (kc & 1) + e]);
-#pragma unroll
-      for (int e = 0; e < 8; e += 4) {
-        const bf16x2 pr0 = {pb[kc][e], pb[kc][e + 1]};
-        const bf16x2 pr1 = {pb[kc][e + 2], pb[kc][e + 3]};
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr0, ones, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr1, ones, ps1, false);
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 pr = {__builtin_amdgcn_exp2f(t[kc >> 1][8 * (kc & 1) + 2 * e]),
+                          __builtin_amdgcn_exp2f(t[kc >> 1][8 * (kc & 1) + 2 * e + 1])};
+        const bf16x2 pk = __builtin_convertvector(pr, bf16x2);
+        w[e] = __builtin_bit_cast(uint32_t, pk);
+        if (e & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ps1, false);
+        else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, ps0, false);
       }
+      pb[kc] = __builtin_bit_cast(bf16x8, w);
     }
     const float psum = ps0 + ps1;
     l_run += psum;
@@ -560,7 +559,7 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t tile = blockIdx.x;   // = (b * H + h) * Tq + i
   const int i = (int)(tile % (uint32_t)p.Tq);
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
