@@ -59,6 +59,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--per-step", action="store_true", help="add per-step times to the JSON")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     return ap.parse_args()
 
 
@@ -84,9 +87,10 @@ def generate(cfg, dev):
     return qs, ks, v
 
 
-def computed_flops(mask, cfg, tiles_q, tiles_k):
-    """Algorithmic flops of one step given the mask at its start: 4 * rows * cols * D summed
-    over the tiles whose bit is clear (valid rows and columns only)."""
+def computed_work(mask, cfg, tiles_q, tiles_k):
+    """Algorithmic work of one step given the mask at its start, over the tiles whose bit is
+    clear (valid rows and columns only): flops 4 * rows * cols * D, K/V bytes requested
+    2 * cols * D * sizeof(dtype), and the skipped-tile fraction."""
     import torch
     n, bq, bk = cfg.seq_len, cfg.tile_q, cfg.tile_k
     dev = mask.device
@@ -95,9 +99,25 @@ def computed_flops(mask, cfg, tiles_q, tiles_k):
     bits = ((words >> (j % 32).to(torch.int32)) & 1).to(torch.float64)          # [B,H,Tq,Tk]
     rows = torch.clamp(n - torch.arange(tiles_q, device=dev) * bq, max=bq).to(torch.float64)
     cols = torch.clamp(n - j * bk, max=bk).to(torch.float64)
-    computed = ((1.0 - bits) * rows[:, None] * cols[None, :]).sum().item()
-    skipped_frac = bits.mean().item()
-    return 4.0 * computed * cfg.head_dim, skipped_frac
+    keep = 1.0 - bits
+    computed = (keep * rows[:, None] * cols[None, :]).sum().item()
+    kv_cols = (keep * cols[None, :]).sum().item()
+    elt = 2 if cfg.dtype == torch.bfloat16 else 4
+    return 4.0 * computed * cfg.head_dim, 2.0 * kv_cols * cfg.head_dim * elt, bits.mean().item()
+
+
+def linear_fit(xs, ys):
+    """Least-squares y = a x + b; returns (a, b, r2)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    if n < 2 or sxx == 0.0:
+        return None, None, None
+    a = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx
+    b = my - a * mx
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    ss_res = sum((y - (a * x + b)) ** 2 for x, y in zip(xs, ys))
+    return a, b, (1.0 - ss_res / ss_tot) if ss_tot > 0 else None
 
 
 def cpu_baseline(cfg, qs, ks, v, budget_s: float):
@@ -157,6 +177,25 @@ def traffic_per_launch(kernel_hash: str, workload: str):
     return entry.get("bytes_per_launch")
 
 
+def copy_calibration(torch):
+    """Plain kernels of known traffic: a fill writes 2^30 bytes, a copy reads and writes 2^30
+    bytes, a sum reads 2^30 bytes (each three times)."""
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        src.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(3):
+        total += float(src.sum())
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration done (checksum {total:.0f})")
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -166,6 +205,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import temporally_sparse_attention_amd as tsa
     from workloads import get_config
 
@@ -218,15 +260,16 @@ def main():
 
     # untimed replay of the same (deterministic) chain for per-step skipped fractions and
     # algorithmic flops of the computed tiles
-    flops, skipped = [], []
+    flops, kv_bytes, skipped = [], [], []
     mask2 = att.new_mask(dev)
     for k_idx in range(warmup + steps):
         t = k_idx % cfg.steps
         if t == 0:
             att.reset_mask(mask2)
         if k_idx >= warmup:
-            f, sfrac = computed_flops(mask2, cfg, tiles_q, tiles_k)
+            f, kvb, sfrac = computed_work(mask2, cfg, tiles_q, tiles_k)
             flops.append(f)
+            kv_bytes.append(kvb)
             skipped.append(sfrac)
         att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
     torch.cuda.synchronize()
@@ -278,6 +321,9 @@ def main():
         },
         "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
         "dense_step_tflops_equiv_per_step": None,
+        "computed_tflops_mean": round(achieved, 2),
+        "kv_gbs_requested_mean": round(sum(kv_bytes) / (sum(kernel_ms) * 1e-3) / 1e9, 1),
+        "time_fit": None,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -285,11 +331,17 @@ def main():
     dense_steps = [kernel_ms[s] for s in range(steps) if (warmup + s) % cfg.steps == 0]
     if dense_steps:
         result["dense_step_tflops_equiv_per_step"] = round(dense / (min(dense_steps) * 1e-3) / 1e12, 2)
+    # time_t ~= t_dense * (1 - s_t) + t0 over the timed steps
+    a, b0, r2 = linear_fit([1.0 - x for x in skipped], kernel_ms)
+    if a is not None:
+        result["time_fit"] = {"t_dense_ms": round(a, 3), "t0_ms": round(b0, 3),
+                              "r2": None if r2 is None else round(r2, 4)}
     if args.per_step:
         result["per_step"] = [
             {"t": (warmup + s) % cfg.steps, "kernel_ms": round(kernel_ms[s], 4),
              "skipped": round(skipped[s], 4),
-             "computed_tflops": round(flops[s] / (kernel_ms[s] * 1e-3) / 1e12, 2)}
+             "computed_tflops": round(flops[s] / (kernel_ms[s] * 1e-3) / 1e12, 2),
+             "kv_gbs_requested": round(kv_bytes[s] / (kernel_ms[s] * 1e-3) / 1e9, 1)}
             for s in range(steps)]
     print(json.dumps(result), flush=True)
 

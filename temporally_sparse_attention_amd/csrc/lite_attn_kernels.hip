@@ -319,77 +319,73 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     }
   };
 
-  // Per-lane LDS read bases within a stage (bytes).
-  // K operand for key block kb, feature step c: key row 32kb + l32, chunk 2c + half.
-  const int k_rd = l32 * G::KROW + 16 * half;
-  // V^T operand for feature block db and 16-key step kc: two transposed 4-row reads at key rows
-  // 16kc + 4*half (+8), columns 32db + 16*(g16 & 1) + 4*(lane & 3) of each 16-lane group g16.
-  const int g16 = lane >> 4, gi = lane & 15;
-  const int v_rd = (4 * half + (gi >> 2)) * G::VROW + 2 * (16 * (g16 & 1) + 4 * (gi & 3));
-
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
-  // MFMA phases read their LDS operands through a ring, several MFMAs ahead of use, so the
-  // LDS latency overlaps the matrix pipe instead of stalling in front of every MFMA; while in
-  // an MFMA phase a wave raises its issue priority so that the other wave on the SIMD fills
-  // the gaps with its softmax work.
-  constexpr int RING = 4;
+  float m_run = -INFINITY;   // running row maximum of raw scores (the QK-Skip reference)
+  float m_ref = -INFINITY;   // exponent reference of the accumulators (lags m_run by < 2^8)
+  float l_run = 0.f;         // this lane's partial row sum
+  const float c2 = p.scale_log2;
+  const float inv_c2 = 1.f / c2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // Software pipeline. Iteration n of the tile loop overlaps the matrix work of one tile with
+  // the vector work of another, so that a wave keeps the MFMA pipe busy while it computes its
+  // own softmax:
+  //   phase A: MFMAs of S^T for tile n+1  ||  exponentials, bf16 packing, row sums of tile n
+  //   phase B: MFMAs of O^T += V^T P^T for tile n  ||  scaling and row maxima of tile n+1
+  // Stages: K(n+1) and V(n) are resident during iteration n; K(n+2) and V(n+1) are loaded into
+  // the other stages meanwhile (the stages they overwrite were last read in iteration n-1,
+  // which the barrier at the top of the iteration has closed).
+
+  // Operand reads. K operand for key block kb, feature step c: key row 32kb + l32, chunk
+  // 2c + half. V^T operand for feature block db and 16-key step kc: two transposed 4-row reads
+  // at key rows 16kc + 4*half (+8), columns 32db + 16*(g16 & 1) + 4*(lane & 3) of each 16-lane
+  // group g16.
+  const int k_rd = l32 * G::KROW + 16 * half;
+  const int g16 = lane >> 4, gi = lane & 15;
+  const int v_rd = (4 * half + (gi >> 2)) * G::VROW + 2 * (16 * (g16 & 1) + 4 * (gi & 3));
+  auto kread = [&](const unsigned char* kst, int t) {   // t -> key block t & 1, feature step t >> 1
+    return *reinterpret_cast<const bf16x8*>(kst + k_rd + (t & 1) * 32 * G::KROW + 32 * (t >> 1));
+  };
+  auto vread = [&](const unsigned char* vst, int t) {   // t -> feature block t % (D/32), keys t / (D/32)
+    const int db = t % (D / 32), kc = t / (D / 32);
+    const unsigned char* base = vst + v_rd + kc * 16 * G::VROW + db * 64;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)base);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 8 * G::VROW));
+    const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
+    bf16x8 av;
+    av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
+    av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
+    return av;
+  };
+  constexpr int RING = 4;   // operand reads in flight ahead of their MFMA
 
   // S^T = K Q^T for keys 32kb + 8(r/4) + 4*half + (r%4) of a tile, query l32 (lane). The 16
-  // MFMAs alternate between the two key blocks.
-  auto qk = [&](const unsigned char* kst, f32x16 (&sc)[2]) {
-    auto kread = [&](int t) {   // t -> key block t & 1, feature step t >> 1
-      return *reinterpret_cast<const bf16x8*>(kst + k_rd + (t & 1) * 32 * G::KROW + 32 * (t >> 1));
-    };
+  // MFMAs alternate between the two key blocks. No scheduling directives: callers interleave.
+  auto qk_mfma = [&](const unsigned char* kst, f32x16 (&sc)[2]) {
     bf16x8 kr[RING];
 #pragma unroll
-    for (int t = 0; t < RING; ++t) kr[t] = kread(t);
+    for (int t = 0; t < RING; ++t) kr[t] = kread(kst, t);
     sc[0] = f32x16{};
     sc[1] = f32x16{};
 #pragma unroll
     for (int t = 0; t < D / 8; ++t) {
       sc[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[t % RING], qf[t >> 1], sc[t & 1], 0, 0, 0);
-      if (t + RING < D / 8) kr[t % RING] = kread(t + RING);
-    }
-    // Keep the ring: RING operand reads up front, then one MFMA and one read at a time.
-    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
-#pragma unroll
-    for (int t = 0; t < D / 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (t + RING < D / 8) kr[t % RING] = kread(kst, t + RING);
     }
   };
-  // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4). Step t
-  // covers feature block t % (D/32) and 16-key step t / (D/32).
-  auto pv = [&](const unsigned char* vst, const bf16x8 (&pb)[4]) {
-    auto vread = [&](int t) {
-      const int db = t % (D / 32), kc = t / (D / 32);
-      const unsigned char* base = vst + v_rd + kc * 16 * G::VROW + db * 64;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)base);
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + 8 * G::VROW));
-      const bf16x4 lo4 = __builtin_bit_cast(bf16x4, lo), hi4 = __builtin_bit_cast(bf16x4, hi);
-      bf16x8 av;
-      av[0] = lo4[0]; av[1] = lo4[1]; av[2] = lo4[2]; av[3] = lo4[3];
-      av[4] = hi4[0]; av[5] = hi4[1]; av[6] = hi4[2]; av[7] = hi4[3];
-      return av;
-    };
+  // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4).
+  auto pv_mfma = [&](const unsigned char* vst, const bf16x8 (&pb)[4]) {
     bf16x8 vr[RING];
 #pragma unroll
-    for (int t = 0; t < RING; ++t) vr[t] = vread(t);
+    for (int t = 0; t < RING; ++t) vr[t] = vread(vst, t);
 #pragma unroll
     for (int t = 0; t < D / 8; ++t) {
       const int db = t % (D / 32), kc = t / (D / 32);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[t % RING], pb[kc], o[db], 0, 0, 0);
-      if (t + RING < D / 8) vr[t % RING] = vread(t + RING);
-    }
-    // Keep the ring: two transposed reads per MFMA operand.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);
-#pragma unroll
-    for (int t = 0; t < D / 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (t + RING < D / 8) vr[t % RING] = vread(vst, t + RING);
     }
   };
   // Keys >= N of the ragged last tile do not exist: their scores become -inf.
@@ -400,70 +396,28 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       for (int r = 0; r < 16; ++r)
         if (j * BK + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3) >= N) sc[kb][r] = -INFINITY;
   };
-
-  float m_run = -INFINITY;   // running row maximum of raw scores (the QK-Skip reference)
-  float m_ref = -INFINITY;   // exponent reference of the accumulators (lags m_run by < 2^8)
-  float l_run = 0.f;         // this lane's partial row sum
-  const float c2 = p.scale_log2;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  const float inv_c2 = 1.f / c2;
-
-  // One visited tile (list position n, key tile j; j_next is the tile at position n + 1): wait
-  // for its K/V stage, start loading the next tile into the other stage, then scores, softmax,
-  // QK-Skip vote and PV.
-  auto tile_step = [&](int n, int j, int j_next, const unsigned char* kcur,
-                       const unsigned char* vcur, unsigned char* knext, unsigned char* vnext) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of tile n landed
-    __syncthreads();                                      // everyone's landed; tile n-1 consumed
-    if (n + 1 < cnt) {
-      issue_k(j_next, knext);
-      issue_v(j_next, vnext);
-    }
-
-    f32x16 sc[2];
-    qk(kcur, sc);
-    if ((j + 1) * BK > N) mask_ragged(j, sc);
-
-    // Scores in exp2 units relative to the exponent reference, t = s * c2 - m_ref * c2. These
-    // are results of arithmetic, so their maximum needs no NaN quieting (taking it on the raw
-    // MFMA results would cost one extra instruction per score); the row maximum in raw units
-    // is recovered from it.
-    const float nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;
-    f32x16 t[2];
+  // Scores to exp2 units relative to the exponent reference, in place (t = s * c2 - m_ref * c2),
+  // and the tile's row maximum in raw units. The maximum is taken on the results of the
+  // arithmetic, which needs no NaN quieting (taking it on the raw MFMA results would cost one
+  // extra instruction per score); the raw maximum is recovered from it. Returns the maximum in
+  // exp2 units through tm.
+  auto scale_max = [&](f32x16 (&s)[2], float nb, float& tm) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[kb][r] = fmaf(sc[kb][r], c2, nb);
-    float tm0 = fmaxf(t[0][0], t[1][0]), tm1 = fmaxf(t[0][1], t[1][1]);
+      for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c2, nb);
+    float tm0 = fmaxf(s[0][0], s[1][0]), tm1 = fmaxf(s[0][1], s[1][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) {
-      tm0 = fmaxf(tm0, fmaxf(t[0][r], t[1][r]));
-      tm1 = fmaxf(tm1, fmaxf(t[0][r + 1], t[1][r + 1]));
+      tm0 = fmaxf(tm0, fmaxf(s[0][r], s[1][r]));
+      tm1 = fmaxf(tm1, fmaxf(s[0][r + 1], s[1][r + 1]));
     }
-    const float tm = halves_max(fmaxf(tm0, tm1));
-    const float mt = (tm - nb) * inv_c2;   // this tile's row maximum of raw scores
-    const float m_prev = m_run;
-    m_run = fmaxf(m_run, mt);
-    // Lazy rescale: move the exponent reference only when some row's maximum exceeds it by
-    // more than 2^8 in exp2 units (or there is no reference yet), so exponentials stay <= 256
-    // and the common case skips the accumulator rescale.
-    if (__ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
-      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
-      const float shift = -m_run * c2 - nb;
-      m_ref = m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[kb][r] += shift;
-    }
-
-    // P as bf16 B operands (16-key step kc: registers 8(kc%2) .. +7 of t[kc/2]) and the row
-    // sum over the same rounded weights (v_dot2 with ones, two partial sums).
-    bf16x8 pb[4];
+    tm = halves_max(fmaxf(tm0, tm1));
+    return (tm - nb) * inv_c2;
+  };
+  // P as bf16 B operands (16-key step kc: registers 8(kc%2) .. +7 of t[kc/2]) and the row sum
+  // over the same rounded weights (v_dot2 with ones, two partial sums).
+  auto exp_pack = [&](const f32x16 (&t)[2], bf16x8 (&pb)[4]) {
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -479,38 +433,112 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       }
       pb[kc] = __builtin_bit_cast(bf16x8, w);
     }
-    const float psum = ps0 + ps1;
-    l_run += psum;
+    return ps0 + ps1;
+  };
+  // Folds the scaled scores s of the tile just scored into the running maximum and, when some
+  // row's maximum exceeds the exponent reference by more than 2^8 in exp2 units (or there is
+  // no reference yet), moves the reference: exponentials then stay <= 256 and the common case
+  // skips the accumulator rescale. `live` is false for the dummy tile after the last one.
+  auto fold_max = [&](f32x16 (&s)[2], float nb, float tm, float mt, bool live) {
+    m_run = fmaxf(m_run, mt);
+    if (live && __ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
+      const float shift = -m_run * c2 - nb;
+      m_ref = m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] += shift;
+    }
+  };
 
-    // QK-Skip vote against the running maximum of the tiles visited before this one: keep the
-    // tile if any valid row is not far enough below it, or has a NaN weight.
-    const float diff = (mt - m_prev) * p.scale;
+  // One iteration: tile n (key tile j, scaled scores in tc, row maximum mt and the running
+  // maximum before it mp) is finished, and tile n+1 (key tile j1, raw scores into tn) is
+  // scored. j2 is the key tile at position n+2 (loaded here). kst: stage holding K(n+1);
+  // kfree: stage to receive K(n+2); vst: stage holding V(n); vfree: stage to receive V(n+1).
+  auto iteration = [&](int n, int j, int j1, int j2, f32x16 (&tc)[2], f32x16 (&tn)[2],
+                       float& mt, float& mp, const unsigned char* kst, unsigned char* kfree,
+                       const unsigned char* vst, unsigned char* vfree) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads have landed
+    __syncthreads();                                      // everyone's; iteration n-1 is done
+    if (n + 2 < cnt) issue_k(j2, kfree);
+    if (n + 1 < cnt) issue_v(j1, vfree);
+    const bool live = n + 1 < cnt;
+
+    // phase A. After the last tile, K(n+1) is a stale stage: its scores are never used.
+    bf16x8 pb[4];
+    qk_mfma(kst, tn);
+    const float psum = exp_pack(tc, pb);
+    l_run += psum;
+    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);    // K operand reads
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);       // VALU / transcendental
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+
+    // QK-Skip vote for tile n against the running maximum of the tiles visited before it: keep
+    // the tile if any valid row is not far enough below it, or has a NaN weight.
+    const float diff = (mt - mp) * p.scale;
     const bool below = !row_valid || (diff < p.log_eps && psum == psum);
     if (__ballot(!below) != 0ull) {
       if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
     }
+    if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
 
-    pv(vcur, pb);
+    // phase B
+    const float nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;
+    pv_mfma(vst, pb);
+    float tm;
+    const float mt1 = scale_max(tn, nb, tm);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);   // V operand reads
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+    mp = m_run;
+    mt = mt1;
+    fold_max(tn, nb, tm, mt1, live);
   };
 
-  // The list entries for the next two positions are read ahead so that the tile index is in a
-  // scalar register when the step begins.
-  int j_cur = cnt > 0 ? __builtin_amdgcn_readfirstlane(s_list[0]) : 0;
-  int j_nxt = cnt > 1 ? __builtin_amdgcn_readfirstlane(s_list[1]) : 0;
+  // Prologue: load K(0), V(0), K(1); score tile 0.
+  f32x16 ta[2], tb[2];
+  float mt = -INFINITY, mp = -INFINITY;
+  int j0 = cnt > 0 ? __builtin_amdgcn_readfirstlane(s_list[0]) : 0;
+  int j1 = cnt > 1 ? __builtin_amdgcn_readfirstlane(s_list[1]) : 0;
+  int j2 = cnt > 2 ? __builtin_amdgcn_readfirstlane(s_list[2]) : 0;
   if (cnt > 0) {
-    issue_k(j_cur, s_k0);
-    issue_v(j_cur, s_v0);
+    issue_k(j0, s_k0);
+    issue_v(j0, s_v0);
+    if (cnt > 1) issue_k(j1, s_k1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    qk_mfma(s_k0, ta);
+    if ((j0 + 1) * BK > N) mask_ragged(j0, ta);
+    const float nb = 0.f;
+    float tm;
+    mt = scale_max(ta, nb, tm);
+    mp = m_run;
+    fold_max(ta, nb, tm, mt, true);
   }
+  // Main loop, unrolled by two so that every stage is named statically. The list entries two
+  // positions ahead are read early so that tile indices are in scalar registers.
   for (int n = 0; n < cnt; n += 2) {
-    int j_after = n + 2 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 2]) : 0;
-    tile_step(n, j_cur, j_nxt, s_k0, s_v0, s_k1, s_v1);
-    j_cur = j_nxt;
-    j_nxt = j_after;
+    int j3 = n + 3 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 3]) : 0;
+    iteration(n, j0, j1, j2, ta, tb, mt, mp, s_k1, s_k0, s_v0, s_v1);
     if (n + 1 < cnt) {
-      j_after = n + 3 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 3]) : 0;
-      tile_step(n + 1, j_cur, j_nxt, s_k1, s_v1, s_k0, s_v0);
-      j_cur = j_nxt;
-      j_nxt = j_after;
+      const int j4 = n + 4 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 4]) : 0;
+      iteration(n + 1, j1, j2, j3, tb, ta, mt, mp, s_k0, s_k1, s_v1, s_v0);
+      j0 = j2;
+      j1 = j3;
+      j2 = j4;
     }
   }
   __syncthreads();
