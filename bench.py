@@ -59,6 +59,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--per-step", action="store_true", help="add per-step times to the JSON")
+    ap.add_argument("--in-step-skip", action="store_true",
+                    help="enable the in-step-skip option (tiles flagged in a step also leave that "
+                         "step's output; their exponentials and PV are not computed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -226,7 +229,8 @@ def main():
     dt_name = "bf16" if cfg.dtype == torch.bfloat16 else "fp32"
     att = tsa.LiteAttention(cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, tile_q=cfg.tile_q,
                             tile_k=cfg.tile_k, dtype=dt_name, softmax_scale=cfg.softmax_scale,
-                            order=cfg.order, dense_prefix=cfg.dense_prefix)
+                            order=cfg.order, dense_prefix=cfg.dense_prefix,
+                            in_step_skip=args.in_step_skip)
     tiles_q, tiles_k = att.tiles
     out = torch.empty_like(qs[0])
     mask = att.new_mask(dev)
@@ -268,10 +272,15 @@ def main():
             att.reset_mask(mask2)
         if k_idx >= warmup:
             f, kvb, sfrac = computed_work(mask2, cfg, tiles_q, tiles_k)
+        att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
+        if k_idx >= warmup:
+            if args.in_step_skip:
+                # tiles flagged during this step were scored (QK) but got no PV product
+                f_after, _, _ = computed_work(mask2, cfg, tiles_q, tiles_k)
+                f = f_after + 0.5 * (f - f_after)
             flops.append(f)
             kv_bytes.append(kvb)
             skipped.append(sfrac)
-        att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
     torch.cuda.synchronize()
     if not torch.equal(mask, mask2):
         log("[bench] warning: replayed mask chain differs from the timed chain")
@@ -318,6 +327,7 @@ def main():
             "head_dim": cfg.head_dim, "tile_q": cfg.tile_q, "tile_k": cfg.tile_k,
             "schedule_steps": cfg.steps, "softmax_scale": cfg.softmax_scale, "order": cfg.order,
             "dense_prefix": cfg.dense_prefix, "parallelism": "single GPU",
+            "in_step_skip": bool(args.in_step_skip),
         },
         "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
         "dense_step_tflops_equiv_per_step": None,

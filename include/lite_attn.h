@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define LITE_ATTN_ABI_VERSION 1
+#define LITE_ATTN_ABI_VERSION 2
 
 typedef enum lite_attn_status {
   LITE_ATTN_OK = 0,
@@ -61,6 +61,18 @@ typedef enum lite_attn_order {
   LITE_ATTN_ORDER_ALT = 1
 } lite_attn_order;
 
+typedef enum lite_attn_option {
+  /* In-step skip. A tile that the QK-Skip test flags while it is visited is also left out of
+   * this step's own output (its exponentials and PV product are not computed), instead of
+   * only from the next step on. The flags, and so the mask after the step, are unchanged (a
+   * flagged tile lies below the running maximum, so leaving it out does not move that
+   * maximum); the output becomes softmax attention over the tiles still clear in the mask
+   * after the step. The left-out softmax mass of a row is at most (left-out columns) times
+   * exp(log_eps_t). LiteAttention, page 1 "Architecture Overview": the skip logic sits inside
+   * the FlashAttention softmax pipeline. */
+  LITE_ATTN_OPT_IN_STEP_SKIP = 1u
+} lite_attn_option;
+
 typedef struct lite_attn_config {
   int32_t abi_version;   /* must be LITE_ATTN_ABI_VERSION */
   int32_t batch;         /* B >= 0 */
@@ -77,6 +89,8 @@ typedef struct lite_attn_config {
   int64_t stride_b;      /* element strides shared by q, k, v, out; all three zero selects */
   int64_t stride_h;      /* the contiguous layout [B][H][N][D]. Each must be a multiple of */
   int64_t stride_n;      /* 8 elements (16 bytes); head_dim <= stride_n < 2^24.            */
+  uint32_t options;      /* OR of lite_attn_option flags; 0 = the plain method */
+  uint32_t reserved;     /* must be 0 */
 } lite_attn_config;
 
 typedef struct lite_attn_s* lite_attn_t;
@@ -84,7 +98,8 @@ typedef struct lite_attn_s* lite_attn_t;
 /* Validate `cfg` and create a handle (host memory only; no device call).
  * LiteAttention, page 1 "Architecture Overview": the Skip-Mask bitmask and QK-Skip.
  * Returns INVALID_ARG for NULL arguments, a wrong abi_version, negative sizes, strides that
- * are not multiples of 8 elements, or dense_prefix outside [0, seq_len]; UNSUPPORTED for a
+ * are not multiples of 8 elements, dense_prefix outside [0, seq_len], unknown option bits or
+ * a nonzero reserved field; UNSUPPORTED for a
  * head_dim / tile / dtype combination without a kernel or for Tk > 2048 (N > 131072 with
  * 64-key tiles). On failure *out is set to NULL. */
 int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out);
@@ -114,8 +129,9 @@ int lite_attn_mask_geometry(lite_attn_t handle, int32_t* tiles_q, int32_t* tiles
  * Each visited tile j is tested: with mt[r] its scaled row maxima and m[r] the running row
  * maxima over tiles visited before it, the tile is flagged when mt[r] - m[r] < log_eps_t for
  * every valid row r of the tile and the tile is not exempt (dense_prefix). Flagged bits are
- * OR-ed into `mask` when the query tile finishes (they take effect from the next step); no
- * bit is ever cleared by this call.
+ * OR-ed into `mask` when the query tile finishes (they take effect from the next step, or,
+ * with LITE_ATTN_OPT_IN_STEP_SKIP, already leave this step's output); no bit is ever cleared
+ * by this call.
  *
  * q, k, v: read-only device tensors (see conventions); out: device tensor written for every
  * valid row, must not alias q, k or v; mask: device words read and updated in place.

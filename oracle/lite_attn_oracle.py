@@ -38,6 +38,12 @@ and tile j is flagged when margin(j) < 0, i.e. when every row's local maximum is
 touch the dense prefix [0, dense_prefix)). A NaN margin never flags. Flags take effect from
 the next step: mask_next = mask | flagged. Bits are never cleared here.
 
+In-step skip (an option, off by default; page 1 "Architecture Overview": the skip logic sits
+inside the softmax pipeline). A tile flagged while it is visited is also left out of this
+step's own output. Flagging never changes the running maximum (a flagged tile's row maxima lie
+below it), so the flags are the same as without the option, and the output is the plain
+definition above taken over the mask *after* the step: A'(i) = tiles clear in mask_next.
+
 Page 1's code sketch expresses the threshold as a ratio on scores; on exponentiated scores the
 ratio test exp(mt) < ratio * exp(m) is exactly mt - m < ln(ratio), which is the log-domain
 budget log_eps used here (page 1 "Architecture Overview", accumulated-error calibration,
@@ -114,7 +120,7 @@ def _head(x, b: int, h: int) -> np.ndarray:
 
 def _row_tile(qi: np.ndarray, kh: np.ndarray, vh: np.ndarray, skipped: np.ndarray, i: int, *,
               tile_q: int, tile_k: int, scale: float, log_eps: float, descending: bool,
-              dense_prefix: int):
+              dense_prefix: int, in_step_skip: bool = False):
     """Output rows, flags and margins of row tile i of one head."""
     n = kh.shape[0]
     tk = skipped.shape[0]
@@ -123,16 +129,6 @@ def _row_tile(qi: np.ndarray, kh: np.ndarray, vh: np.ndarray, skipped: np.ndarra
 
     # Scaled scores of these rows against every key (float64).
     s = scale * (qi @ kh.T)                                   # [nr, N]
-
-    # Output: softmax over the allowed columns only.
-    allowed_cols = np.repeat(~skipped, tile_k)[:n]
-    if allowed_cols.any():
-        sa = np.where(allowed_cols[None, :], s, -np.inf)
-        row_max = sa.max(axis=1, keepdims=True)
-        p = np.exp(sa - row_max)
-        out = (p @ vh) / p.sum(axis=1, keepdims=True)
-    else:
-        out = np.zeros((nr, dv))
 
     # Per-row maximum of each key tile (padding columns of the ragged last tile are -inf).
     padded = np.full((nr, tk * tile_k), -np.inf)
@@ -155,12 +151,25 @@ def _row_tile(qi: np.ndarray, kh: np.ndarray, vh: np.ndarray, skipped: np.ndarra
         if margin < 0 and not (row_exempt or col_exempt):
             flags[j] = True
         running = np.maximum(running, mt)
+
+    # Output: softmax over the allowed columns only (with in-step skip, tiles flagged in this
+    # step are not allowed either).
+    out_skipped = (skipped | flags) if in_step_skip else skipped
+    allowed_cols = np.repeat(~out_skipped, tile_k)[:n]
+    if allowed_cols.any():
+        sa = np.where(allowed_cols[None, :], s, -np.inf)
+        row_max = sa.max(axis=1, keepdims=True)
+        p = np.exp(sa - row_max)
+        out = (p @ vh) / p.sum(axis=1, keepdims=True)
+    else:
+        out = np.zeros((nr, dv))
     return out, flags, margins
 
 
 def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale: float,
                        log_eps: float, step: int, order: str = "alt", dense_prefix: int = 0,
-                       rows: Optional[Iterable[Tuple[int, int, int]]] = None) -> StepResult:
+                       rows: Optional[Iterable[Tuple[int, int, int]]] = None,
+                       in_step_skip: bool = False) -> StepResult:
     """One denoising step of LiteAttention on [B, H, N, D] inputs.
 
     q, k, v: numpy arrays or torch CPU tensors [B, H, N, D] (any float dtype).
@@ -169,6 +178,7 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
              descending on odd steps).
     rows:    optional (b, h, i) row tiles to evaluate; default every row tile. Rows of the
              output not evaluated are NaN; mask rows not evaluated are copied unchanged.
+    in_step_skip: also leave the tiles flagged in this step out of this step's output.
     """
     if order not in ("asc", "alt"):
         raise ValueError("order must be 'asc' or 'alt'")
@@ -200,7 +210,7 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
             o, flags, marg = _row_tile(qh[r0:r1], kh, vh, skipped_all[b, h, i], i,
                                        tile_q=tile_q, tile_k=tile_k, scale=softmax_scale,
                                        log_eps=log_eps, descending=descending,
-                                       dense_prefix=dense_prefix)
+                                       dense_prefix=dense_prefix, in_step_skip=in_step_skip)
             out[b, h, r0:r1] = o
             margins[b, h, i] = marg
             computed[b, h, i] = True
@@ -210,7 +220,8 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
 
 def run_chain_ref(inputs_for_step, steps: int, log_eps_schedule, *, batch: int, heads: int,
                   seq_len: int, tile_q: int, tile_k: int, softmax_scale: float,
-                  order: str = "alt", dense_prefix: int = 0, rows=None):
+                  order: str = "alt", dense_prefix: int = 0, rows=None,
+                  in_step_skip: bool = False):
     """Run `steps` denoising steps from an empty mask. inputs_for_step(t) -> (q, k, v).
     Yields (t, mask_at_start, StepResult) per step."""
     mask = empty_mask(batch, heads, seq_len, tile_q, tile_k)
@@ -218,6 +229,7 @@ def run_chain_ref(inputs_for_step, steps: int, log_eps_schedule, *, batch: int, 
         q, k, v = inputs_for_step(t)
         res = lite_attn_step_ref(q, k, v, mask, tile_q=tile_q, tile_k=tile_k,
                                  softmax_scale=softmax_scale, log_eps=log_eps_schedule[t],
-                                 step=t, order=order, dense_prefix=dense_prefix, rows=rows)
+                                 step=t, order=order, dense_prefix=dense_prefix, rows=rows,
+                                 in_step_skip=in_step_skip)
         yield t, mask, res
         mask = res.mask_next

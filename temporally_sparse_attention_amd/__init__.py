@@ -11,6 +11,7 @@ from __future__ import annotations
 from .binding import (  # noqa: F401
     ABI_VERSION,
     EXPORTS,
+    OPT_IN_STEP_SKIP,
     LIB_PATH,
     Handle,
     LiteAttnError,

@@ -14,7 +14,8 @@ from typing import Optional, Tuple
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblite_attn.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
+OPT_IN_STEP_SKIP = 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = range(5)
 DTYPES = {"bf16": 0, "fp32": 1}
 ORDERS = {"asc": 0, "alt": 1}
@@ -49,6 +50,8 @@ class LiteAttnConfig(ctypes.Structure):
         ("stride_b", ctypes.c_int64),
         ("stride_h", ctypes.c_int64),
         ("stride_n", ctypes.c_int64),
+        ("options", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -162,14 +165,16 @@ class Handle:
 def make_config(batch: int, heads: int, seq_len: int, head_dim: int, *, tile_q: int = 128,
                 tile_k: int = 64, dtype: str = "bf16", softmax_scale: float = 0.0,
                 order: str = "alt", dense_prefix: int = 0,
-                strides: Tuple[int, int, int] = (0, 0, 0)) -> LiteAttnConfig:
+                strides: Tuple[int, int, int] = (0, 0, 0),
+                in_step_skip: bool = False) -> LiteAttnConfig:
     if dtype not in DTYPES:
         raise ValueError(f"dtype must be one of {list(DTYPES)}")
     if order not in ORDERS:
         raise ValueError(f"order must be one of {list(ORDERS)}")
     return LiteAttnConfig(ABI_VERSION, batch, heads, seq_len, head_dim, tile_q, tile_k,
                           DTYPES[dtype], float(softmax_scale), ORDERS[order], dense_prefix,
-                          int(strides[0]), int(strides[1]), int(strides[2]))
+                          int(strides[0]), int(strides[1]), int(strides[2]),
+                          OPT_IN_STEP_SKIP if in_step_skip else 0, 0)
 
 
 def lite_attn_create(batch: int, heads: int, seq_len: int, head_dim: int, **kw) -> Handle:

@@ -78,6 +78,9 @@ int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
                   c.dense_prefix, c.seq_len);
     if (!(std::isfinite(c.softmax_scale)))
       return fail(LITE_ATTN_ERR_INVALID_ARG, "create: softmax_scale is not finite");
+    if ((c.options & ~(uint32_t)LITE_ATTN_OPT_IN_STEP_SKIP) != 0u || c.reserved != 0u)
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "create: unknown option bits 0x%x or reserved %u",
+                  c.options, c.reserved);
 
     int64_t sb = c.stride_b, sh = c.stride_h, sn = c.stride_n;
     if (sb == 0 && sh == 0 && sn == 0) {
@@ -94,7 +97,8 @@ int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
     if (c.tile_k != lite_attn::kTileK)
       return fail(LITE_ATTN_ERR_UNSUPPORTED, "create: tile_k %d not built (only %d)", c.tile_k,
                   lite_attn::kTileK);
-    lite_attn::FwdLauncher fwd = lite_attn::get_fwd_launcher(c.dtype, c.head_dim, c.tile_q);
+    const bool in_step = (c.options & LITE_ATTN_OPT_IN_STEP_SKIP) != 0u;
+    lite_attn::FwdLauncher fwd = lite_attn::get_fwd_launcher(c.dtype, c.head_dim, c.tile_q, in_step);
     if (!fwd)
       return fail(LITE_ATTN_ERR_UNSUPPORTED,
                   "create: no kernel for dtype=%d head_dim=%d tile_q=%d (built: head_dim 64/128,"

@@ -29,9 +29,9 @@ struct FwdParams {
 
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
 
-// Launcher for (dtype, head_dim, tile_q) or nullptr when no kernel is built for it.
-// dtype: 0 = bf16, 1 = fp32.
-FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q);
+// Launcher for (dtype, head_dim, tile_q, in-step skip) or nullptr when no kernel is built for
+// it. dtype: 0 = bf16, 1 = fp32.
+FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q, bool in_step_skip);
 
 hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream);
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,

@@ -63,11 +63,18 @@ __device__ __forceinline__ uint32_t low_bits(int w, int jp) {
   return rem >= 32 ? 0xffffffffu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
 }
 
+// IEEE 754-2019 maximum: a NaN operand gives NaN (v_maximum3_f32 on gfx950). Row maxima use it,
+// so that a NaN score makes the row's maximum, and with it the QK-Skip margin, NaN: such a tile
+// is never flagged.
+__device__ __forceinline__ float nanmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Value of x in the other half-wave (lane ^ 32) combined with x by max / sum.
 __device__ __forceinline__ float halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nanmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -193,19 +200,22 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // 16 bytes per lane from the buffer at byte offset voff straight into LDS: lane l's data lands
-// at lds_addr + 16 * l. Issued as inline assembly so that the compiler does not track these
-// loads as LDS writes: the kernel orders them itself (each wave waits for its own loads with
-// s_waitcnt vmcnt(0) before the workgroup barrier that precedes any read of the stage), and
-// the compiler would otherwise make unrelated LDS accesses wait for every load in flight. The
-// instruction has no register result, and M0 is declared clobbered.
-__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_addr, uint32_t voff) {
+// at lds_a + lds_b + 16 * l. Issued as inline assembly so that the compiler does not track
+// these loads as LDS writes: the kernel orders them itself (each wave waits for its own loads
+// with s_waitcnt vmcnt(0) before the workgroup barrier that precedes any read of the stage),
+// and the compiler would otherwise make unrelated LDS accesses wait for every load in flight.
+// The LDS address is summed into M0 inside the block (a per-wave base plus a constant), which
+// keeps the many loop-invariant addresses out of scalar registers. The instruction has no
+// register result, and M0 is declared clobbered.
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_a, uint32_t lds_b,
+                                          uint32_t voff) {
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_add_u32 m0, %0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds"
       :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory", "m0");
+      : "s"(lds_a), "s"(lds_b), "v"(voff), "s"(rsrc)
+      : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
@@ -213,7 +223,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 #endif
 
-template <int D, int NW>
+template <int D, int NW, bool INSTEP>
 __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using G = Bf16TileGeom<D>;
@@ -295,27 +305,28 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     const int row = slot / G::VCH, ch = slot % G::VCH;
     voff[n] = ch < G::CH ? (uint32_t)row * row_bytes + 16u * ch : kOobOffset;
   }
+  const uint32_t wave1k = 1024u * wave;   // this wave's first 1 KB slot of a stage
   auto tile_bytes = [&](int key0) {
     return (uint32_t)(min(BK, N - key0) - 1) * row_bytes + D * 2;
   };
   auto issue_k = [&](int j, unsigned char* dst) {
     const int key0 = j * BK;
     const i32x4 r = make_rsrc(kh + (int64_t)key0 * sn, tile_bytes(key0));
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(dst));
+    const uint32_t base = lds_address(dst);
 #pragma unroll
     for (int n = 0; n < KLOADS; ++n) {
       const int x = wave + NW * n;
-      if (KLOADS * NW == G::KCH || x < G::KCH) lds_dma16(r, base + x * 1024, koff[n]);
+      if (KLOADS * NW == G::KCH || x < G::KCH) lds_dma16(r, wave1k, base + NW * n * 1024, koff[n]);
     }
   };
   auto issue_v = [&](int j, unsigned char* dst) {
     const int key0 = j * BK;
     const i32x4 r = make_rsrc(vh + (int64_t)key0 * sn, tile_bytes(key0));
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(dst));
+    const uint32_t base = lds_address(dst);
 #pragma unroll
     for (int n = 0; n < VLOADS; ++n) {
       const int x = wave + NW * n;
-      if (VLOADS * NW == G::VCH || x < G::VCH) lds_dma16(r, base + x * 1024, voff[n]);
+      if (VLOADS * NW == G::VCH || x < G::VCH) lds_dma16(r, wave1k, base + NW * n * 1024, voff[n]);
     }
   };
 
@@ -406,13 +417,15 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fmaf(s[kb][r], c2, nb);
-    float tm0 = fmaxf(s[0][0], s[1][0]), tm1 = fmaxf(s[0][1], s[1][1]);
+    // two chains of three-input maxima (v_maximum3_f32): 16 instructions for 32 scores
+    float tm0 = nanmax(nanmax(s[0][0], s[1][0]), s[0][2]);
+    float tm1 = nanmax(nanmax(s[0][1], s[1][1]), s[1][2]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) {
-      tm0 = fmaxf(tm0, fmaxf(s[0][r], s[1][r]));
-      tm1 = fmaxf(tm1, fmaxf(s[0][r + 1], s[1][r + 1]));
+    for (int r = 3; r < 16; r += 2) {
+      tm0 = nanmax(nanmax(tm0, s[0][r]), s[1][r]);
+      if (r + 1 < 16) tm1 = nanmax(nanmax(tm1, s[0][r + 1]), s[1][r + 1]);
     }
-    tm = halves_max(fmaxf(tm0, tm1));
+    tm = halves_max(nanmax(tm0, tm1));
     return (tm - nb) * inv_c2;
   };
   // P as bf16 B operands (16-key step kc: registers 8(kc%2) .. +7 of t[kc/2]) and the row sum
@@ -440,7 +453,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   // no reference yet), moves the reference: exponentials then stay <= 256 and the common case
   // skips the accumulator rescale. `live` is false for the dummy tile after the last one.
   auto fold_max = [&](f32x16 (&s)[2], float nb, float tm, float mt, bool live) {
-    m_run = fmaxf(m_run, mt);
+    m_run = nanmax(m_run, mt);
     if (live && __ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
       const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
       const float shift = -m_run * c2 - nb;
@@ -459,6 +472,39 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   // maximum before it mp) is finished, and tile n+1 (key tile j1, raw scores into tn) is
   // scored. j2 is the key tile at position n+2 (loaded here). kst: stage holding K(n+1);
   // kfree: stage to receive K(n+2); vst: stage holding V(n); vfree: stage to receive V(n+1).
+  // QK-Skip vote for a tile against the running maximum of the tiles visited before it (mp):
+  // the wave keeps the tile if any of its valid rows is not far enough below (a NaN margin
+  // keeps); the workgroup's keep bits are OR-ed in LDS.
+  auto vote = [&](int j, float mt, float mp) {
+    const float diff = (mt - mp) * p.scale;
+    const bool below = !row_valid || diff < p.log_eps;
+    if (__ballot(!below) != 0ull) {
+      if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
+    }
+  };
+  const bool row_exempt = i * BQ < p.dense_prefix;
+  const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
+
+  auto phase_a_sched = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);    // K operand reads
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);       // VALU / transcendental
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+  };
+  auto phase_b_sched = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);   // V operand reads
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+  };
+
   auto iteration = [&](int n, int j, int j1, int j2, f32x16 (&tc)[2], f32x16 (&tn)[2],
                        float& mt, float& mp, const unsigned char* kst, unsigned char* kfree,
                        const unsigned char* vst, unsigned char* vfree) {
@@ -468,43 +514,45 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     if (n + 1 < cnt) issue_v(j1, vfree);
     const bool live = n + 1 < cnt;
 
-    // phase A. After the last tile, K(n+1) is a stale stage: its scores are never used.
-    bf16x8 pb[4];
-    qk_mfma(kst, tn);
-    const float psum = exp_pack(tc, pb);
-    l_run += psum;
-    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);    // K operand reads
-    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);       // VALU / transcendental
-#pragma unroll
-    for (int t = 0; t < D / 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    // With in-step skip, tile n's votes were cast when it was scored (previous iteration) and
+    // the barrier above has closed them: a flagged tile gets no exponentials and no PV.
+    bool skip = false;
+    if constexpr (INSTEP) {
+      const uint32_t kw = __builtin_amdgcn_readfirstlane(s_keep[j >> 5]);
+      skip = !((kw >> (j & 31)) & 1u) && !row_exempt && j >= exempt_cols;
     }
 
-    // QK-Skip vote for tile n against the running maximum of the tiles visited before it: keep
-    // the tile if any valid row is not far enough below it, or has a NaN weight.
-    const float diff = (mt - mp) * p.scale;
-    const bool below = !row_valid || (diff < p.log_eps && psum == psum);
-    if (__ballot(!below) != 0ull) {
-      if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
-    }
-    if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
-
-    // phase B
-    const float nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;
-    pv_mfma(vst, pb);
-    float tm;
-    const float mt1 = scale_max(tn, nb, tm);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);   // V operand reads
+    float nb, tm, mt1;
+    if (!skip) {
+      // phase A. After the last tile, K(n+1) is a stale stage: its scores are never used.
+      bf16x8 pb[4];
+      qk_mfma(kst, tn);
+      l_run += exp_pack(tc, pb);
+      phase_a_sched();
+      if constexpr (!INSTEP) vote(j, mt, mp);
+      if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
+      // phase B
+      nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
+      pv_mfma(vst, pb);
+      mt1 = scale_max(tn, nb, tm);
+      phase_b_sched();
+    } else {
+      qk_mfma(kst, tn);
+      __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
 #pragma unroll
-    for (int t = 0; t < D / 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      for (int t = 0; t < D / 8; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
+      nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;
+      mt1 = scale_max(tn, nb, tm);
     }
     mp = m_run;
     mt = mt1;
+    if constexpr (INSTEP) {
+      if (live) vote(j1, mt1, mp);
+    }
     fold_max(tn, nb, tm, mt1, live);
   };
 
@@ -526,6 +574,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     float tm;
     mt = scale_max(ta, nb, tm);
     mp = m_run;
+    if constexpr (INSTEP) vote(j0, mt, mp);
     fold_max(ta, nb, tm, mt, true);
   }
   // Main loop, unrolled by two so that every stage is named statically. The list entries two
@@ -559,15 +608,14 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       }
   }
 
-  const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
-  write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, i * BQ < p.dense_prefix, exempt_cols);
+  write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, row_exempt, exempt_cols);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 // ---------------------------------------------------------------------------------------
 // fp32 kernel: MFMA 32x32x2 f32, single-buffered (the fp32 workload is small).
 // ---------------------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool INSTEP>
 __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
@@ -656,9 +704,9 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
     }
     float mt = s[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
+    for (int r = 1; r < 16; ++r) mt = nanmax(mt, s[0][r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
+    for (int r = 0; r < 16; ++r) mt = nanmax(mt, s[1][r]);
     mt = halves_max(mt);
 
     const float diff = (mt - m_run) * p.scale;
@@ -666,8 +714,17 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
     if (__ballot(!below) != 0ull) {
       if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
     }
+    if constexpr (INSTEP) {
+      // the workgroup's votes on this tile are complete after the barrier; a flagged tile
+      // (which lies below the running maximum, so m is unchanged) is left out of this output
+      __syncthreads();
+      const uint32_t kw = __builtin_amdgcn_readfirstlane(s_keep[j >> 5]);
+      if (!((kw >> (j & 31)) & 1u) && !(i * BQ < p.dense_prefix) &&
+          j >= (p.dense_prefix + BK - 1) / BK)
+        continue;
+    }
 
-    const float m_new = fmaxf(m_run, mt);
+    const float m_new = nanmax(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
     const float nb = -m_new * c2;
     float psum = 0.f;
@@ -743,39 +800,45 @@ __global__ void __launch_bounds__(256) mask_popcount(const uint32_t* mask, uint3
 
 // hipLaunchKernel reports the status of this launch only (hipGetLastError would also return
 // errors left behind by other HIP users in the process).
-template <int D, int NW>
+template <int D, int NW, bool INSTEP>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.Tq);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_bf16<D, NW>), dim3(grid),
-                         dim3(NW * 64), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_bf16<D, NW, INSTEP>),
+                         dim3(grid), dim3(NW * 64), args, 0, stream);
 }
 
-template <int D, int NW>
+template <int D, int NW, bool INSTEP>
 hipError_t launch_f32(const FwdParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.Tq);
   FwdParams arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_f32<D, NW>), dim3(grid),
-                         dim3(NW * 64), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_f32<D, NW, INSTEP>),
+                         dim3(grid), dim3(NW * 64), args, 0, stream);
+}
+
+template <bool INSTEP>
+FwdLauncher pick_launcher(int dtype, int head_dim, int tile_q) {
+  if (dtype == 0) {
+    if (head_dim == 128 && tile_q == 128) return &launch_bf16<128, 4, INSTEP>;
+    if (head_dim == 128 && tile_q == 64) return &launch_bf16<128, 2, INSTEP>;
+    if (head_dim == 64 && tile_q == 128) return &launch_bf16<64, 4, INSTEP>;
+    if (head_dim == 64 && tile_q == 64) return &launch_bf16<64, 2, INSTEP>;
+  } else if (dtype == 1) {
+    if (head_dim == 128 && tile_q == 128) return &launch_f32<128, 4, INSTEP>;
+    if (head_dim == 128 && tile_q == 64) return &launch_f32<128, 2, INSTEP>;
+    if (head_dim == 64 && tile_q == 128) return &launch_f32<64, 4, INSTEP>;
+    if (head_dim == 64 && tile_q == 64) return &launch_f32<64, 2, INSTEP>;
+  }
+  return nullptr;
 }
 
 }  // namespace
 
-FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q) {
-  if (dtype == 0) {
-    if (head_dim == 128 && tile_q == 128) return &launch_bf16<128, 4>;
-    if (head_dim == 128 && tile_q == 64) return &launch_bf16<128, 2>;
-    if (head_dim == 64 && tile_q == 128) return &launch_bf16<64, 4>;
-    if (head_dim == 64 && tile_q == 64) return &launch_bf16<64, 2>;
-  } else if (dtype == 1) {
-    if (head_dim == 128 && tile_q == 128) return &launch_f32<128, 4>;
-    if (head_dim == 128 && tile_q == 64) return &launch_f32<128, 2>;
-    if (head_dim == 64 && tile_q == 128) return &launch_f32<64, 4>;
-    if (head_dim == 64 && tile_q == 64) return &launch_f32<64, 2>;
-  }
-  return nullptr;
+FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q, bool in_step_skip) {
+  return in_step_skip ? pick_launcher<true>(dtype, head_dim, tile_q)
+                      : pick_launcher<false>(dtype, head_dim, tile_q);
 }
 
 hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream) {

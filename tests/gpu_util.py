@@ -81,13 +81,13 @@ def make_attention(cfg, **over):
 
 
 def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=None,
-                         scale=None, label="", log_eps=None):
+                         scale=None, label="", log_eps=None, in_step_skip=False):
     """Run `steps` steps. Before each step the GPU mask rows under test are overwritten with
     the oracle's mask; outputs and new mask rows are compared on `rows` (default: all)."""
     dev = workload.device
     order = order or cfg.order
     scale = cfg.softmax_scale if scale is None else scale
-    att = att or make_attention(cfg, order=order, softmax_scale=scale)
+    att = att or make_attention(cfg, order=order, softmax_scale=scale, in_step_skip=in_step_skip)
     tq, tk = att.tiles
     B, H = cfg.batch, cfg.heads
     ref_mask = np.zeros(att.mask_shape, dtype=np.uint32)
@@ -125,7 +125,8 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
                                        tile_q=att.handle.cfg.tile_q, tile_k=cfg.tile_k,
                                        softmax_scale=scale, log_eps=le, step=t, order=order,
                                        dense_prefix=cfg.dense_prefix,
-                                       rows=[(0, 0, i) for i in tiles])
+                                       rows=[(0, 0, i) for i in tiles],
+                                       in_step_skip=in_step_skip)
                 for i in tiles:
                     r0, r1 = i * att.handle.cfg.tile_q, min(cfg.seq_len, (i + 1) * att.handle.cfg.tile_q)
                     ref_out[b, h, r0:r1] = r.out[0, 0, r0:r1]
@@ -142,7 +143,8 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
         else:
             ref = lite_attn_step_ref(qc, kc, vc, ref_mask, tile_q=att.handle.cfg.tile_q,
                                      tile_k=cfg.tile_k, softmax_scale=scale, log_eps=le, step=t,
-                                     order=order, dense_prefix=cfg.dense_prefix)
+                                     order=order, dense_prefix=cfg.dense_prefix,
+                                     in_step_skip=in_step_skip)
             cmp.add_out(out.double().cpu().numpy(), ref.out)
             cmp.add_mask(mask_to_bits(from_mask_tensor(gpu_mask), tk),
                          mask_to_bits(ref.mask_next, tk), ref.margins,

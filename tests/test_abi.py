@@ -51,13 +51,16 @@ def test_config_struct_layout_matches_c(tmp_path):
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "lite_attn.h"\n'
                    'int main(void){ printf("%zu %zu %zu %zu\\n", sizeof(lite_attn_config),'
                    ' offsetof(lite_attn_config, softmax_scale), offsetof(lite_attn_config, dense_prefix),'
-                   ' offsetof(lite_attn_config, stride_b)); return 0; }\n')
+                   ' offsetof(lite_attn_config, stride_b)); printf("%zu %zu %d\\n",'
+                   ' offsetof(lite_attn_config, options), offsetof(lite_attn_config, reserved),'
+                   ' (int)LITE_ATTN_OPT_IN_STEP_SKIP); return 0; }\n')
     exe = tmp_path / "off"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()
     c = binding.LiteAttnConfig
     assert [int(x) for x in got] == [ctypes.sizeof(c), c.softmax_scale.offset,
-                                     c.dense_prefix.offset, c.stride_b.offset]
+                                     c.dense_prefix.offset, c.stride_b.offset, c.options.offset,
+                                     c.reserved.offset, binding.OPT_IN_STEP_SKIP]
 
 
 def _status(fn):
@@ -81,6 +84,12 @@ def test_create_validation():
     assert _status(ok(strides=(0, 0, 100))) == binding.ERR_INVALID_ARG     # not a multiple of 8
     assert _status(ok(strides=(0, 0, 64))) == binding.ERR_INVALID_ARG      # < head_dim
     assert _status(lambda: tsa.lite_attn_create(1, 1, 140000, 64, tile_q=128)) == binding.ERR_UNSUPPORTED
+    assert _status(ok(in_step_skip=True)) == binding.OK
+    assert _status(ok(in_step_skip=True, dtype="fp32", tile_q=64)) == binding.OK
+    for field, value in (("options", 2), ("options", 0x80000001), ("reserved", 1)):
+        bad = tsa.make_config(1, 2, 1000, 128)
+        setattr(bad, field, value)
+        assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=bad)) == binding.ERR_INVALID_ARG
     cfg = tsa.make_config(1, 2, 1000, 128)
     cfg.abi_version = 99
     assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=cfg)) == binding.ERR_INVALID_ARG

@@ -290,3 +290,76 @@ def test_rejects_bad_arguments_and_empty_inputs():
     r = lite_attn_step_ref(e, e, e, empty_mask(1, 1, 0, 2, 2), tile_q=2, tile_k=2,
                            softmax_scale=1.0, log_eps=-1.0, step=0)
     assert r.out.shape == (1, 1, 0, 2) and r.mask_next.shape == (1, 1, 0, 0)
+
+
+# ------------------------------------------------------------------ in-step skip variant
+@pytest.mark.parametrize("seed", range(12))
+def test_in_step_skip_output_is_block_masked_attention_over_next_mask(seed):
+    """With in-step skip the flags are those of the plain step (brute force), and the output is
+    block-masked softmax attention over the tiles still clear after the step (closed form,
+    pure-Python attention)."""
+    rng = np.random.default_rng(5000 + seed)
+    n = int(rng.integers(4, 36))
+    d = int(rng.integers(1, 5))
+    tq = int(rng.choice([1, 2, 3, 4, 8]))
+    tk = int(rng.choice([1, 2, 3, 4, 8]))
+    scale = float(rng.choice([1.0, 2.5]))
+    log_eps = float(rng.choice([-0.5, -2.0, -4.0]))
+    step = int(rng.integers(0, 4))
+    order = str(rng.choice(["asc", "alt"]))
+    prefix = int(rng.choice([0, 0, 3]))
+    q, k, v = _rand(rng, n, d, 2.0), _rand(rng, n, d, 2.0), _rand(rng, n, 2)
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    skipped = rng.random((tqn, tkn)) < float(rng.choice([0.0, 0.3]))
+    mask = bits_to_mask(skipped)[None, None]
+    kw = dict(tile_q=tq, tile_k=tk, softmax_scale=scale, log_eps=log_eps, step=step,
+              order=order, dense_prefix=prefix)
+    plain = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, **kw)
+    res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, in_step_skip=True, **kw)
+    descending = order == "alt" and step % 2 == 1
+    flags, _ = pyref.brute_flags(q, k, skipped.tolist(), tq, tk, scale, log_eps, descending, prefix)
+    after = skipped | np.asarray(flags, dtype=bool)
+    assert np.array_equal(mask_to_bits(res.mask_next, tkn)[0, 0], after)
+    assert np.array_equal(res.mask_next, plain.mask_next)
+    np.testing.assert_array_equal(np.nan_to_num(res.margins, nan=7.0), np.nan_to_num(plain.margins, nan=7.0))
+    allowed = [[not after[r // tq, c // tk] for c in range(n)] for r in range(n)]
+    want = np.array(pyref.masked_attention(q, k, v, allowed, scale))
+    for i in range(tqn):
+        rows = slice(i * tq, min(n, (i + 1) * tq))
+        if after[i].all():
+            assert np.all(res.out[0, 0, rows] == 0)
+        else:
+            np.testing.assert_allclose(res.out[0, 0, rows], want[rows], rtol=1e-12, atol=1e-12)
+
+
+def test_in_step_skip_changes_output_by_at_most_the_flagged_mass():
+    """Leaving out tiles whose scores all lie more than |log_eps| below the row's running
+    maximum moves each output row by at most 2 * w * max|v|, where w is the softmax mass of the
+    left-out columns (bounded by their count times exp(log_eps)); and without flags the two
+    modes agree exactly."""
+    rng = np.random.default_rng(77)
+    n, d, tq, tk = 48, 3, 8, 4
+    x = np.linspace(0, 1, n)[:, None]
+    q = np.hstack([np.cos(6 * x), np.sin(6 * x), 0.1 * rng.standard_normal((n, 1))]) * 3
+    k = q + 0.05 * rng.standard_normal((n, d))
+    v = rng.standard_normal((n, 2))
+    mask = empty_mask(1, 1, n, tq, tk)
+    kw = dict(tile_q=tq, tile_k=tk, softmax_scale=1.0, step=0, order="asc")
+    for log_eps in (-6.0, -3.0):
+        plain = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=log_eps, **kw)
+        ins = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=log_eps,
+                                 in_step_skip=True, **kw)
+        flagged = mask_to_bits(plain.mask_next, -(-n // tk))[0, 0]
+        assert flagged.any()
+        s = q @ k.T
+        for r in range(n):
+            cols = np.repeat(flagged[r // tq], tk)[:n]
+            p = np.exp(s[r] - s[r].max())
+            w = p[cols].sum() / p.sum()
+            assert w <= cols.sum() * math.exp(log_eps) + 1e-15
+            diff = np.abs(ins.out[0, 0, r] - plain.out[0, 0, r]).max()
+            assert diff <= 2 * w * np.abs(v).max() + 1e-12
+    same = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=-math.inf,
+                              in_step_skip=True, **kw)
+    base = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=-math.inf, **kw)
+    assert np.array_equal(same.out, base.out)
