@@ -59,6 +59,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--per-step", action="store_true", help="add per-step times to the JSON")
+    ap.add_argument("--schedule", action="store_true",
+                    help="use lite_attn_step_scheduled (heaviest-first query-tile order; the "
+                         "scheduling kernel is inside the timed step)")
     ap.add_argument("--in-step-skip", action="store_true",
                     help="enable the in-step-skip option (tiles flagged in a step also leave that "
                          "step's output; their exponentials and PV are not computed)")
@@ -235,6 +238,7 @@ def main():
     out = torch.empty_like(qs[0])
     mask = att.new_mask(dev)
     stream = torch.cuda.current_stream(dev)
+    workspace = att.new_workspace(dev) if args.schedule else None
 
     def run_step(k_idx, ev=None):
         t = k_idx % cfg.steps
@@ -242,7 +246,7 @@ def main():
             att.reset_mask(mask)
         if ev is not None:
             ev[0].record(stream)
-        att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t)
+        att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, workspace=workspace)
         if ev is not None:
             ev[1].record(stream)
 
@@ -327,7 +331,7 @@ def main():
             "head_dim": cfg.head_dim, "tile_q": cfg.tile_q, "tile_k": cfg.tile_k,
             "schedule_steps": cfg.steps, "softmax_scale": cfg.softmax_scale, "order": cfg.order,
             "dense_prefix": cfg.dense_prefix, "parallelism": "single GPU",
-            "in_step_skip": bool(args.in_step_skip),
+            "in_step_skip": bool(args.in_step_skip), "schedule": bool(args.schedule),
         },
         "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
         "dense_step_tflops_equiv_per_step": None,

@@ -143,6 +143,26 @@ int lite_attn_mask_geometry(lite_attn_t handle, int32_t* tiles_q, int32_t* tiles
 int lite_attn_step(lite_attn_t handle, const void* q, const void* k, const void* v, void* out,
                    uint32_t* mask, float log_eps_t, int32_t step, void* stream);
 
+/* Bytes of device workspace that lite_attn_step_scheduled needs: about 6 * B * H * Tq, in
+ * 256-byte units (0 for a NULL handle). */
+size_t lite_attn_workspace_bytes(lite_attn_t handle);
+
+/* lite_attn_step with a heaviest-first schedule: same arguments, same results (bit for bit),
+ * plus a caller-owned device `workspace` of lite_attn_workspace_bytes(handle) bytes, 256-byte
+ * aligned, that the call overwrites (it holds nothing between calls). A first kernel reads the
+ * mask and counts, per query tile, the key tiles it will visit (its skip-list length). Query
+ * tiles that visit at least half of all key tiles and at least four times the mean (dense
+ * prefix rows in a sparse step, for example) are scheduled first; every other tile keeps its
+ * natural order, which keeps neighbouring query tiles together. The attention kernel then runs
+ * its workgroups in that order, so that long query tiles do not start last and set the step's
+ * tail. LiteAttention, page 1 "Architecture Overview": the skip list used at high sparsity;
+ * here its list lengths drive the schedule. Calls that share a workspace must be ordered on
+ * one stream. Returns what lite_attn_step returns, and INVALID_ARG for a NULL or misaligned
+ * workspace. */
+int lite_attn_step_scheduled(lite_attn_t handle, const void* q, const void* k, const void* v,
+                             void* out, uint32_t* mask, float log_eps_t, int32_t step,
+                             void* workspace, void* stream);
+
 /* Clear every word of `mask` (a new generation starts dense). LiteAttention, page 1
  * "Architecture Overview": decisions persist until the attention distribution shifts; this
  * is the explicit way to drop them. Uses a fill kernel (no memset node), so it may be

@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     lite_attn_reset_mask,
     lite_attn_status_string,
     lite_attn_step,
+    lite_attn_step_scheduled,
+    lite_attn_workspace_bytes,
     make_config,
 )
 from .schedule import ErrorBudgetSchedule  # noqa: F401
@@ -59,8 +61,19 @@ class LiteAttention:
     def reset_mask(self, mask, stream=None):
         lite_attn_reset_mask(self.handle, mask, stream)
 
-    def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None):
-        lite_attn_step(self.handle, q, k, v, out, mask, log_eps_t, step, stream)
+    def new_workspace(self, device):
+        """Device workspace for scheduled steps (heaviest-first query-tile order)."""
+        import torch
+        return torch.empty(max(1, lite_attn_workspace_bytes(self.handle)), dtype=torch.uint8,
+                           device=device)
+
+    def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None, workspace=None):
+        """One denoising step; with a workspace, the query tiles run heaviest first."""
+        if workspace is None:
+            lite_attn_step(self.handle, q, k, v, out, mask, log_eps_t, step, stream)
+        else:
+            lite_attn_step_scheduled(self.handle, q, k, v, out, mask, log_eps_t, step, workspace,
+                                     stream)
 
     def popcount(self, mask, counts=None, stream=None):
         """Per-head skipped-tile counts (device int32 [B*H]); asynchronous."""

@@ -27,6 +27,8 @@ EXPORTS = (
     "lite_attn_mask_bytes",
     "lite_attn_mask_geometry",
     "lite_attn_step",
+    "lite_attn_workspace_bytes",
+    "lite_attn_step_scheduled",
     "lite_attn_reset_mask",
     "lite_attn_mask_popcount",
     "lite_attn_status_string",
@@ -101,6 +103,11 @@ def _load() -> ctypes.CDLL:
     lib.lite_attn_mask_geometry.restype = ctypes.c_int
     lib.lite_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32, vp]
     lib.lite_attn_step.restype = ctypes.c_int
+    lib.lite_attn_workspace_bytes.argtypes = [vp]
+    lib.lite_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.lite_attn_step_scheduled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
+                                             vp, vp]
+    lib.lite_attn_step_scheduled.restype = ctypes.c_int
     lib.lite_attn_reset_mask.argtypes = [vp, vp, vp]
     lib.lite_attn_reset_mask.restype = ctypes.c_int
     lib.lite_attn_mask_popcount.argtypes = [vp, vp, vp, vp]
@@ -273,6 +280,33 @@ def lite_attn_step(handle: Handle, q, k, v, out, mask, log_eps_t: float, step: i
                                ctypes.c_float(log_eps_t), ctypes.c_int32(step),
                                ctypes.c_void_p(st)),
            "lite_attn_step")
+
+
+def lite_attn_workspace_bytes(handle: Handle) -> int:
+    return int(_lib.lite_attn_workspace_bytes(handle.ptr))
+
+
+def lite_attn_step_scheduled(handle: Handle, q, k, v, out, mask, log_eps_t: float, step: int,
+                             workspace, stream=None):
+    """lite_attn_step with a heaviest-first schedule; `workspace` is a device tensor of at least
+    lite_attn_workspace_bytes(handle) bytes, 256-byte aligned."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _check_qkvo(handle, t, name)
+    _check_mask(handle, mask)
+    torch = _torch()
+    if isinstance(workspace, torch.Tensor):
+        if (not workspace.is_contiguous() or
+                workspace.numel() * workspace.element_size() < lite_attn_workspace_bytes(handle)):
+            raise ValueError("workspace must be a contiguous tensor of at least "
+                             f"{lite_attn_workspace_bytes(handle)} bytes")
+    dev = None if isinstance(q, int) else q.device
+    st = _stream_ptr(stream, dev)
+    _check(_lib.lite_attn_step_scheduled(handle.ptr, _ptr(q, "q", dev), _ptr(k, "k", dev),
+                                         _ptr(v, "v", dev), _ptr(out, "out", dev),
+                                         _ptr(mask, "mask", dev), ctypes.c_float(log_eps_t),
+                                         ctypes.c_int32(step), _ptr(workspace, "workspace", dev),
+                                         ctypes.c_void_p(st)),
+           "lite_attn_step_scheduled")
 
 
 def lite_attn_reset_mask(handle: Handle, mask, stream=None):

@@ -149,24 +149,33 @@ int lite_attn_mask_geometry(lite_attn_t h, int32_t* tiles_q, int32_t* tiles_k,
   return LITE_ATTN_OK;
 }
 
-int lite_attn_step(lite_attn_t h, const void* q, const void* k, const void* v, void* out,
-                   uint32_t* mask, float log_eps_t, int32_t step, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of lite_attn_step and lite_attn_step_scheduled.
+int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, const void* v,
+              void* out, uint32_t* mask, float log_eps_t, int32_t step, void* workspace,
+              bool scheduled, void* stream) {
   try {
-    if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "step: NULL handle");
+    if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL handle", who);
     if (std::isnan(log_eps_t) || log_eps_t > 0.f)
-      return fail(LITE_ATTN_ERR_INVALID_ARG, "step: log_eps_t must be in [-inf, 0], got %g",
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: log_eps_t must be in [-inf, 0], got %g", who,
                   (double)log_eps_t);
-    if (step < 0) return fail(LITE_ATTN_ERR_INVALID_ARG, "step: negative step %d", step);
+    if (step < 0) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: negative step %d", who, step);
     const lite_attn_config& c = h->cfg;
     if ((int64_t)c.batch * c.heads * c.seq_len == 0) return LITE_ATTN_OK;
     if (!q || !k || !v || !out || !mask)
-      return fail(LITE_ATTN_ERR_INVALID_ARG, "step: NULL tensor or mask pointer");
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL tensor or mask pointer", who);
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(mask, 4))
-      return fail(LITE_ATTN_ERR_INVALID_ARG, "step: misaligned pointer (tensors need 16 B)");
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: misaligned pointer (tensors need 16 B)", who);
     if (out == q || out == k || out == v)
-      return fail(LITE_ATTN_ERR_INVALID_ARG, "step: out aliases an input");
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: out aliases an input", who);
+    if (scheduled && (!workspace || !aligned(workspace, 256)))
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or not 256-byte aligned workspace", who);
 
+    const hipStream_t st = static_cast<hipStream_t>(stream);
     lite_attn::FwdParams p;
     p.q = q;
     p.k = k;
@@ -187,13 +196,43 @@ int lite_attn_step(lite_attn_t h, const void* q, const void* k, const void* v, v
     p.log_eps = log_eps_t;
     p.descending = (c.order == LITE_ATTN_ORDER_ALT && (step & 1)) ? 1 : 0;
     p.dense_prefix = c.dense_prefix;
-    const hipError_t e = h->fwd(p, static_cast<hipStream_t>(stream));
+    p.perm = nullptr;
+    if (scheduled) {
+      const int n = c.batch * c.heads * h->Tq;
+      const hipError_t e = lite_attn::launch_plan(mask, n, h->W, h->Tk, workspace, st);
+      if (e != hipSuccess)
+        return fail(LITE_ATTN_ERR_HIP, "%s: schedule launch failed: %s", who,
+                    hipGetErrorString(e));
+      p.perm = static_cast<const uint32_t*>(workspace);
+    }
+    const hipError_t e = h->fwd(p, st);
     if (e != hipSuccess)
-      return fail(LITE_ATTN_ERR_HIP, "step: kernel launch failed: %s", hipGetErrorString(e));
+      return fail(LITE_ATTN_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
     return LITE_ATTN_OK;
   } catch (...) {
-    return fail(LITE_ATTN_ERR_HIP, "step: unexpected exception");
+    return fail(LITE_ATTN_ERR_HIP, "%s: unexpected exception", who);
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int lite_attn_step(lite_attn_t h, const void* q, const void* k, const void* v, void* out,
+                   uint32_t* mask, float log_eps_t, int32_t step, void* stream) {
+  return step_impl("step", h, q, k, v, out, mask, log_eps_t, step, nullptr, false, stream);
+}
+
+size_t lite_attn_workspace_bytes(lite_attn_t h) {
+  if (!h) return 0;
+  return lite_attn::plan_workspace_bytes((int64_t)h->cfg.batch * h->cfg.heads * h->Tq);
+}
+
+int lite_attn_step_scheduled(lite_attn_t h, const void* q, const void* k, const void* v,
+                             void* out, uint32_t* mask, float log_eps_t, int32_t step,
+                             void* workspace, void* stream) {
+  return step_impl("step_scheduled", h, q, k, v, out, mask, log_eps_t, step, workspace, true,
+                   stream);
 }
 
 int lite_attn_reset_mask(lite_attn_t h, uint32_t* mask, void* stream) {

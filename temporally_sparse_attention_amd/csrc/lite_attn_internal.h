@@ -25,6 +25,7 @@ struct FwdParams {
   float log_eps;      // QK-Skip budget in natural-log units (may be -inf)
   int descending;     // traversal direction of this step
   int dense_prefix;   // tokens [0, dense_prefix) are exempt from flagging
+  const uint32_t* perm;   // block -> query tile (B*H*Tq entries), or nullptr for the identity
 };
 
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
@@ -34,6 +35,12 @@ using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
 FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q, bool in_step_skip);
 
 hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream);
+
+// Heaviest-first schedule of the query tiles of a mask: the workspace receives the block ->
+// tile permutation (n_tiles uint32 at offset 0) and scratch bucket bytes after it.
+size_t plan_workspace_bytes(int64_t n_tiles);
+hipError_t launch_plan(const uint32_t* mask, int n_tiles, int W, int Tk, void* workspace,
+                       hipStream_t stream);
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,
                                 int Tq, int Tk, int W, hipStream_t stream);
 

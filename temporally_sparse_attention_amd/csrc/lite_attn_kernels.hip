@@ -247,11 +247,12 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Block index = logical tile (b * H + h) * Tq + i. Workgroups are dispatched to the 8 XCDs
-  // round-robin, so each XCD receives every 8th query tile of every head: an even share of
-  // every head and of every region of a head, which keeps the XCDs balanced when skip
-  // densities differ, while all XCDs stream the same head's K/V (it stays in the MALL).
-  const uint32_t tile = blockIdx.x;
+  // Block index = logical tile (b * H + h) * Tq + i, unless a schedule permutes them.
+  // Workgroups are dispatched to the 8 XCDs round-robin, so each XCD receives every 8th query
+  // tile of every head: an even share of every head and of every region of a head, which keeps
+  // the XCDs balanced when skip densities differ, while all XCDs stream the same head's K/V
+  // (it stays in the MALL).
+  const uint32_t tile = p.perm ? p.perm[blockIdx.x] : blockIdx.x;
   const int i = (int)(tile % (uint32_t)p.Tq);
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
@@ -635,7 +636,7 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const uint32_t tile = blockIdx.x;   // = (b * H + h) * Tq + i
+  const uint32_t tile = p.perm ? p.perm[blockIdx.x] : blockIdx.x;   // (b * H + h) * Tq + i
   const int i = (int)(tile % (uint32_t)p.Tq);
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
@@ -783,6 +784,78 @@ __global__ void __launch_bounds__(256) mask_fill_zero(uint32_t* mask, size_t wor
     mask[w] = 0u;
 }
 
+// Heaviest-first schedule (LiteAttention, page 1 "Architecture Overview": a skip list for high
+// sparsity; its list lengths are the per-tile work). A first kernel counts, per query tile, the
+// key tiles it will visit. A single workgroup of 1024 threads then orders the tiles: a tile is
+// heavy when it visits at least half of all key tiles and at least four times the mean count (a
+// dense prefix row in a sparse step, say). Heavy tiles go first, then every other tile, each
+// group in natural order: the long workgroups then start first instead of setting the tail,
+// while neighbouring query tiles (which share K/V through the caches) still run together. Each
+// thread takes a contiguous range of tiles, and a scan over (group, thread) gives every tile
+// its position.
+constexpr int kPlanThreads = 1024;
+
+// Per query tile: the number of key tiles it will visit (one thread per tile).
+__global__ void __launch_bounds__(256) plan_count(const uint32_t* mask, int n, int W, int Tk,
+                                                  uint16_t* count) {
+  const int x = blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  const uint32_t* row = mask + (size_t)x * W;
+  int c = 0;
+  for (int w = 0; w < W; ++w) c += __popc(~row[w] & valid_bits(w, Tk));
+  count[x] = (uint16_t)c;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_heaviest_first(const uint16_t* count, int n,
+                                                                    int Tk, uint32_t* perm) {
+  __shared__ uint32_t s_cnt[2 * kPlanThreads];   // [group][thread], group 0: heavy
+  __shared__ uint32_t s_part[kPlanThreads];
+  __shared__ unsigned long long s_total;
+  const int t = threadIdx.x;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  if (t == 0) s_total = 0ull;
+  __syncthreads();
+  unsigned long long sum = 0ull;
+  for (int x = lo; x < hi; ++x) sum += count[x];
+  atomicAdd(&s_total, sum);
+  __syncthreads();
+  // heavy: c >= Tk / 2 and c * n >= 4 * total (exact integer form of "4 x the mean")
+  const unsigned long long total = s_total;
+  auto heavy = [&](int c) {
+    return 2 * c >= Tk && (unsigned long long)c * (unsigned long long)n >= 4ull * total;
+  };
+  uint32_t nh = 0u, nr = 0u;
+  for (int x = lo; x < hi; ++x) {
+    if (heavy(count[x])) ++nh;
+    else ++nr;
+  }
+  s_cnt[t] = nh;
+  s_cnt[kPlanThreads + t] = nr;
+  __syncthreads();
+  // exclusive scan over the 2 * 1024 counts in [group][thread] order: thread t scans its two
+  // consecutive entries, then the 1024 partial sums are scanned
+  const uint32_t e0 = s_cnt[2 * t], e1 = s_cnt[2 * t + 1];
+  s_part[t] = e0 + e1;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const uint32_t v = t >= off ? s_part[t - off] : 0u;
+    __syncthreads();
+    s_part[t] += v;
+    __syncthreads();
+  }
+  const uint32_t base = s_part[t] - (e0 + e1);
+  __syncthreads();
+  s_cnt[2 * t] = base;
+  s_cnt[2 * t + 1] = base + e0;
+  __syncthreads();
+  uint32_t at_heavy = s_cnt[t], at_rest = s_cnt[kPlanThreads + t];
+  for (int x = lo; x < hi; ++x) {
+    if (heavy(count[x])) perm[at_heavy++] = (uint32_t)x;
+    else perm[at_rest++] = (uint32_t)x;
+  }
+}
+
 __global__ void __launch_bounds__(256) mask_popcount(const uint32_t* mask, uint32_t* counts,
                                                      int Tq, int Tk, int W) {
   __shared__ uint32_t s_sum;
@@ -848,6 +921,27 @@ hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t strea
   void* args[] = {&mask, &words};
   return hipLaunchKernel(reinterpret_cast<const void*>(&mask_fill_zero), dim3((unsigned)blocks),
                          dim3(256), args, 0, stream);
+}
+
+size_t plan_workspace_bytes(int64_t n_tiles) {
+  return ((size_t)n_tiles * 4 + 255) / 256 * 256 + ((size_t)n_tiles * 2 + 255) / 256 * 256;
+}
+
+hipError_t launch_plan(const uint32_t* mask, int n_tiles, int W, int Tk, void* workspace,
+                       hipStream_t stream) {
+  if (n_tiles == 0) return hipSuccess;
+  uint32_t* perm = static_cast<uint32_t*>(workspace);
+  uint16_t* count = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
+                                                ((size_t)n_tiles * 4 + 255) / 256 * 256);
+  void* cargs[] = {&mask, &n_tiles, &W, &Tk, &count};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&plan_count),
+                                 dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), cargs, 0,
+                                 stream);
+  if (e != hipSuccess) return e;
+  const uint16_t* ccount = count;
+  void* args[] = {&ccount, &n_tiles, &Tk, &perm};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&plan_heaviest_first), dim3(1),
+                         dim3(kPlanThreads), args, 0, stream);
 }
 
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total, int Tq,

@@ -122,6 +122,15 @@ def test_step_host_validation_makes_no_device_call():
     assert lib.lite_attn_step(None, p, p, p, p, ms, ctypes.c_float(-1.0), 0, None) == binding.ERR_INVALID_ARG
     assert lib.lite_attn_reset_mask(h.ptr, None, None) == binding.ERR_INVALID_ARG
     assert lib.lite_attn_mask_popcount(h.ptr, ms, None, None) == binding.ERR_INVALID_ARG
+    sc = lambda ws, *a: lib.lite_attn_step_scheduled(h.ptr, p, p, p, ctypes.c_void_p(8192), ms,
+                                                    ctypes.c_float(-1.0), 0, ws, None)
+    assert sc(None) == binding.ERR_INVALID_ARG                          # no workspace
+    assert sc(ctypes.c_void_p(4096 + 128)) == binding.ERR_INVALID_ARG    # not 256-byte aligned
+    assert lib.lite_attn_step_scheduled(h.ptr, p, p, p, ctypes.c_void_p(8192), ms,
+                                        ctypes.c_float(0.5), 0, p, None) == binding.ERR_INVALID_ARG
+    n = 1 * 1 * 2   # B * H * Tq for N = 100, tile_q = 64
+    assert tsa.lite_attn_workspace_bytes(h) >= 6 * n and tsa.lite_attn_workspace_bytes(h) % 256 == 0
+    assert lib.lite_attn_workspace_bytes(None) == 0
     # an empty problem is a no-op that needs no pointers
     e = tsa.lite_attn_create(1, 0, 100, 64, tile_q=64)
     assert lib.lite_attn_step(e.ptr, None, None, None, None, None, ctypes.c_float(-1.0), 0, None) == binding.OK

@@ -1,0 +1,89 @@
+"""Heaviest-first scheduling (lite_attn_step_scheduled): the same results as lite_attn_step, bit
+for bit, and the documented tile order (heavy query tiles first, then the rest, each group in
+natural order)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import device, from_mask_tensor, log, make_attention
+from oracle import mask_to_bits
+from workloads import Workload, derive, get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def expected_order(mask_np: np.ndarray, tiles_k: int) -> np.ndarray:
+    """Reference tile order for a mask [B, H, Tq, W]: tiles visiting at least half of all key
+    tiles and at least four times the mean first, then the others, each in natural order."""
+    bits = mask_to_bits(mask_np, tiles_k).reshape(-1, tiles_k)
+    count = (tiles_k - bits.sum(axis=1)).astype(np.int64)
+    heavy = (2 * count >= tiles_k) & (count * count.size >= 4 * count.sum())
+    return np.argsort(~heavy, kind="stable")
+
+
+CASES = [
+    ("sched_stress", 5, dict(heads=[0, 9, 10], grid=(2, 16, 32)), 5),
+    ("sched_hunyuan_prefix", 4, dict(heads=[0, 1], grid=(2, 9, 40), prefix=256, dense_prefix=256), 4),
+    ("sched_tiny_fp32", 1, {}, 4),
+]
+
+
+@pytest.mark.parametrize("label,cid,kw,steps", CASES, ids=[c[0] for c in CASES])
+def test_scheduled_step_matches_plain_step(label, cid, kw, steps):
+    dev = device()
+    cfg = derive(get_config(cid), name=label, steps=steps, **kw) if kw else get_config(cid)
+    wl = Workload(cfg, dev)
+    att = make_attention(cfg)
+    tq, tk = att.tiles
+    ws = att.new_workspace(dev)
+    m_plain, m_sched = att.new_mask(dev), att.new_mask(dev)
+    n = cfg.batch * cfg.heads * tq
+    for t in range(steps):
+        q, k, v = wl.inputs(t)
+        o_plain, o_sched = torch.empty_like(q), torch.empty_like(q)
+        start = from_mask_tensor(m_sched)
+        att.step(q, k, v, o_plain, m_plain, cfg.log_eps[t], t)
+        att.step(q, k, v, o_sched, m_sched, cfg.log_eps[t], t, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o_plain, o_sched), f"{label} step {t}: outputs differ"
+        assert torch.equal(m_plain, m_sched), f"{label} step {t}: masks differ"
+        perm = ws[:4 * n].view(torch.int32).cpu().numpy()
+        assert np.array_equal(perm, expected_order(start, tk)), f"{label} step {t}: order"
+        log(f"  [{label}] step {t}: first tiles {perm[:6].tolist()}")
+
+
+def test_scheduled_full_size_order_and_result():
+    """At the HunyuanVideo shape (dense prefix rows never skip), one sparse step: the prefix
+    query tiles of every head come first, and the results equal the plain step."""
+    dev = device()
+    cfg = get_config(4)
+    wl = Workload(cfg, dev)
+    att = make_attention(cfg)
+    tq, tk = att.tiles
+    ws = att.new_workspace(dev)
+    mask = att.new_mask(dev)
+    for t in range(2):
+        q, k, v = wl.inputs(t)
+        out = torch.empty_like(q)
+        att.step(q, k, v, out, mask, cfg.log_eps[t], t)
+    q, k, v = wl.inputs(2)
+    m1, m2 = mask.clone(), mask.clone()
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    start = from_mask_tensor(m2)
+    att.step(q, k, v, o1, m1, cfg.log_eps[2], 2)
+    att.step(q, k, v, o2, m2, cfg.log_eps[2], 2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(m1, m2)
+    n = cfg.batch * cfg.heads * tq
+    perm = ws[:4 * n].view(torch.int32).cpu().numpy()
+    assert np.array_equal(perm, expected_order(start, tk))
+    # the prefix query tiles (rows [0, 256) of every head) are never skipped, so in a sparse
+    # step they are heavy and run first
+    bits = mask_to_bits(start, tk).reshape(-1, tk)
+    count = (tk - bits.sum(axis=1)).astype(np.int64)
+    n_heavy = int(((2 * count >= tk) & (count * count.size >= 4 * count.sum())).sum())
+    prefix_tiles = [h * tq + i for h in range(cfg.heads) for i in range(2)]
+    log(f"  heavy tiles: {n_heavy}")
+    assert set(prefix_tiles) <= set(perm[:n_heavy].tolist())
+    wl.drop_cache()
+    torch.cuda.empty_cache()
