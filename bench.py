@@ -62,6 +62,9 @@ def parse_args():
     ap.add_argument("--schedule", action="store_true",
                     help="use lite_attn_step_scheduled (heaviest-first query-tile order; the "
                          "scheduling kernel is inside the timed step)")
+    ap.add_argument("--refresh-delta", type=float, default=None,
+                    help="use lite_attn_step_refresh with this divergence budget (mask rows whose "
+                         "statistic moves by more are cleared)")
     ap.add_argument("--in-step-skip", action="store_true",
                     help="enable the in-step-skip option (tiles flagged in a step also leave that "
                          "step's output; their exponentials and PV are not computed)")
@@ -239,14 +242,25 @@ def main():
     mask = att.new_mask(dev)
     stream = torch.cuda.current_stream(dev)
     workspace = att.new_workspace(dev) if args.schedule else None
+    refresh = args.refresh_delta is not None
+    if refresh and args.schedule:
+        sys.exit("--schedule and --refresh-delta do not combine")
+    stats = att.new_tile_stats(dev) if refresh else None
+    stats2 = att.new_tile_stats(dev) if refresh else None
 
     def run_step(k_idx, ev=None):
         t = k_idx % cfg.steps
         if t == 0:
             att.reset_mask(mask)
+            if refresh:
+                stats.fill_(float("nan"))
         if ev is not None:
             ev[0].record(stream)
-        att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, workspace=workspace)
+        if refresh:
+            att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, tile_stats=stats,
+                     refresh_delta=args.refresh_delta)
+        else:
+            att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, workspace=workspace)
         if ev is not None:
             ev[1].record(stream)
 
@@ -274,9 +288,15 @@ def main():
         t = k_idx % cfg.steps
         if t == 0:
             att.reset_mask(mask2)
+            if refresh:
+                stats2.fill_(float("nan"))
         if k_idx >= warmup:
             f, kvb, sfrac = computed_work(mask2, cfg, tiles_q, tiles_k)
-        att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
+        if refresh:
+            att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t, tile_stats=stats2,
+                     refresh_delta=args.refresh_delta)
+        else:
+            att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
         if k_idx >= warmup:
             if args.in_step_skip:
                 # tiles flagged during this step were scored (QK) but got no PV product
@@ -332,6 +352,7 @@ def main():
             "schedule_steps": cfg.steps, "softmax_scale": cfg.softmax_scale, "order": cfg.order,
             "dense_prefix": cfg.dense_prefix, "parallelism": "single GPU",
             "in_step_skip": bool(args.in_step_skip), "schedule": bool(args.schedule),
+            "refresh_delta": args.refresh_delta,
         },
         "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
         "dense_step_tflops_equiv_per_step": None,

@@ -143,6 +143,29 @@ int lite_attn_mask_geometry(lite_attn_t handle, int32_t* tiles_q, int32_t* tiles
 int lite_attn_step(lite_attn_t handle, const void* q, const void* k, const void* v, void* out,
                    uint32_t* mask, float log_eps_t, int32_t step, void* stream);
 
+/* lite_attn_step with divergence-triggered refresh of mask rows. LiteAttention, page 1
+ * "Core Concept" (the mask is updated only when the attention pattern diverges significantly)
+ * and "Architecture Overview" (decisions carry forward unless the attention distribution
+ * shifts significantly).
+ *
+ * tile_stats: caller-owned device float array [B][H][Tq] (same tile order as the mask), one
+ * reference per query tile; NaN means "no reference" (fill it with NaN when a generation
+ * starts, together with lite_attn_reset_mask). After the tile loop each query tile computes
+ * its statistic: the mean over its valid rows of the largest scaled score over the key tiles it
+ * computed (the running row maximum). If the reference is NaN, the statistic becomes the
+ * reference and the mask row is updated as in lite_attn_step. Otherwise, if the statistic has
+ * moved by more than refresh_delta from the reference (or the move is NaN), the reference is set
+ * to NaN and the row's mask bits are all cleared, so the next step computes the row densely and
+ * flags afresh; else the row is updated as usual and the reference kept. A row maximum falls
+ * when attention moves into skipped tiles, which the mask alone cannot notice. With this call
+ * bits can clear; refresh_delta = +inf never clears (the mask evolves as with lite_attn_step).
+ * The output of the step is that of lite_attn_step (the refresh acts on the mask only).
+ * Returns what lite_attn_step returns, and INVALID_ARG for a NULL or misaligned tile_stats or a
+ * negative or NaN refresh_delta. */
+int lite_attn_step_refresh(lite_attn_t handle, const void* q, const void* k, const void* v,
+                           void* out, uint32_t* mask, float* tile_stats, float refresh_delta,
+                           float log_eps_t, int32_t step, void* stream);
+
 /* Bytes of device workspace that lite_attn_step_scheduled needs: about 6 * B * H * Tq, in
  * 256-byte units (0 for a NULL handle). */
 size_t lite_attn_workspace_bytes(lite_attn_t handle);

@@ -44,6 +44,17 @@ step's own output. Flagging never changes the running maximum (a flagged tile's 
 below it), so the flags are the same as without the option, and the output is the plain
 definition above taken over the mask *after* the step: A'(i) = tiles clear in mask_next.
 
+Divergence-triggered refresh (an option; page 1 "Core Concept": the mask is updated only when
+the attention pattern diverges significantly; "Architecture Overview": decisions carry forward
+unless the attention distribution shifts significantly). The statistic of a row tile is the mean
+over its valid rows of the running row maximum at the end of the step (the largest scaled score
+over the key tiles it computed). A reference is taken on the first step that has none (stored as
+NaN). When the statistic later moves by more than refresh_delta from the reference - or the
+difference is NaN - the tile's mask row is cleared instead of updated (the next step computes
+it densely and flags afresh) and the reference is dropped (NaN); otherwise the row is updated as
+usual and the reference kept. A row maximum falls when the mass moves into skipped tiles, which
+is exactly the divergence the skip mask cannot see.
+
 Page 1's code sketch expresses the threshold as a ratio on scores; on exponentiated scores the
 ratio test exp(mt) < ratio * exp(m) is exactly mt - m < ln(ratio), which is the log-domain
 budget log_eps used here (page 1 "Architecture Overview", accumulated-error calibration,
@@ -107,6 +118,9 @@ class StepResult:
     mask_next: np.ndarray  # [B, H, Tq, W] uint32
     margins: np.ndarray    # [B, H, Tq, Tk] float64; NaN where the tile was not visited
     computed_rows: np.ndarray  # [B, H, Tq] bool: which row tiles were evaluated
+    stats: Optional[np.ndarray] = None        # [B, H, Tq] refresh statistic of this step
+    stats_next: Optional[np.ndarray] = None   # [B, H, Tq] reference after the step (NaN: none)
+    refreshed: Optional[np.ndarray] = None    # [B, H, Tq] bool: row cleared by the refresh
 
 
 def _head(x, b: int, h: int) -> np.ndarray:
@@ -154,6 +168,7 @@ def _row_tile(qi: np.ndarray, kh: np.ndarray, vh: np.ndarray, skipped: np.ndarra
 
     # Output: softmax over the allowed columns only (with in-step skip, tiles flagged in this
     # step are not allowed either).
+    stat = float(np.mean(running))   # refresh statistic: mean of the rows' running maxima
     out_skipped = (skipped | flags) if in_step_skip else skipped
     allowed_cols = np.repeat(~out_skipped, tile_k)[:n]
     if allowed_cols.any():
@@ -163,13 +178,14 @@ def _row_tile(qi: np.ndarray, kh: np.ndarray, vh: np.ndarray, skipped: np.ndarra
         out = (p @ vh) / p.sum(axis=1, keepdims=True)
     else:
         out = np.zeros((nr, dv))
-    return out, flags, margins
+    return out, flags, margins, stat
 
 
 def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale: float,
                        log_eps: float, step: int, order: str = "alt", dense_prefix: int = 0,
                        rows: Optional[Iterable[Tuple[int, int, int]]] = None,
-                       in_step_skip: bool = False) -> StepResult:
+                       in_step_skip: bool = False, tile_stats: Optional[np.ndarray] = None,
+                       refresh_delta: float = math.inf) -> StepResult:
     """One denoising step of LiteAttention on [B, H, N, D] inputs.
 
     q, k, v: numpy arrays or torch CPU tensors [B, H, N, D] (any float dtype).
@@ -179,6 +195,8 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
     rows:    optional (b, h, i) row tiles to evaluate; default every row tile. Rows of the
              output not evaluated are NaN; mask rows not evaluated are copied unchanged.
     in_step_skip: also leave the tiles flagged in this step out of this step's output.
+    tile_stats: float [B, H, Tq] references of the divergence refresh (NaN: none yet), or None
+             for no refresh; refresh_delta: the largest move of the statistic that keeps a row.
     """
     if order not in ("asc", "alt"):
         raise ValueError("order must be 'asc' or 'alt'")
@@ -192,6 +210,16 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
         raise ValueError(f"mask shape {mask.shape} != {(bsz, nh, tq, w)}")
     descending = order == "alt" and step % 2 == 1
 
+    refresh = tile_stats is not None
+    if refresh:
+        tile_stats = np.asarray(tile_stats, dtype=np.float64)
+        if tile_stats.shape != (bsz, nh, tq):
+            raise ValueError(f"tile_stats shape {tile_stats.shape} != {(bsz, nh, tq)}")
+        if not (refresh_delta >= 0.0):
+            raise ValueError("refresh_delta must be >= 0")
+        stats = np.full((bsz, nh, tq), np.nan)
+        stats_next = tile_stats.copy()
+        refreshed = np.zeros((bsz, nh, tq), dtype=bool)
     out = np.full((bsz, nh, n, dv), np.nan)
     mask_next = mask.copy()
     margins = np.full((bsz, nh, tq, tk), np.nan)
@@ -207,14 +235,27 @@ def lite_attn_step_ref(q, k, v, mask, *, tile_q: int, tile_k: int, softmax_scale
         qh, kh, vh = _head(q, b, h), _head(k, b, h), _head(v, b, h)
         for i in tiles:
             r0, r1 = i * tile_q, min(n, (i + 1) * tile_q)
-            o, flags, marg = _row_tile(qh[r0:r1], kh, vh, skipped_all[b, h, i], i,
-                                       tile_q=tile_q, tile_k=tile_k, scale=softmax_scale,
-                                       log_eps=log_eps, descending=descending,
-                                       dense_prefix=dense_prefix, in_step_skip=in_step_skip)
+            o, flags, marg, stat = _row_tile(qh[r0:r1], kh, vh, skipped_all[b, h, i], i,
+                                             tile_q=tile_q, tile_k=tile_k, scale=softmax_scale,
+                                             log_eps=log_eps, descending=descending,
+                                             dense_prefix=dense_prefix,
+                                             in_step_skip=in_step_skip)
             out[b, h, r0:r1] = o
             margins[b, h, i] = marg
             computed[b, h, i] = True
             mask_next[b, h, i] = mask[b, h, i] | bits_to_mask(flags)
+            if refresh:
+                stats[b, h, i] = stat
+                ref = tile_stats[b, h, i]
+                if math.isnan(ref):
+                    stats_next[b, h, i] = stat
+                elif not (abs(stat - ref) <= refresh_delta):
+                    mask_next[b, h, i] = 0          # valid bits cleared, reserved bits stay 0
+                    stats_next[b, h, i] = np.nan
+                    refreshed[b, h, i] = True
+    if refresh:
+        return StepResult(out=out, mask_next=mask_next, margins=margins, computed_rows=computed,
+                          stats=stats, stats_next=stats_next, refreshed=refreshed)
     return StepResult(out=out, mask_next=mask_next, margins=margins, computed_rows=computed)
 
 

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     lite_attn_reset_mask,
     lite_attn_status_string,
     lite_attn_step,
+    lite_attn_step_refresh,
     lite_attn_step_scheduled,
     lite_attn_workspace_bytes,
     make_config,
@@ -67,9 +68,24 @@ class LiteAttention:
         return torch.empty(max(1, lite_attn_workspace_bytes(self.handle)), dtype=torch.uint8,
                            device=device)
 
-    def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None, workspace=None):
-        """One denoising step; with a workspace, the query tiles run heaviest first."""
-        if workspace is None:
+    def new_tile_stats(self, device):
+        """References of the divergence refresh (float32 [B, H, Tq], NaN: none yet)."""
+        import torch
+        c = self.handle.cfg
+        return torch.full((c.batch, c.heads, self.handle.tiles_q), float("nan"),
+                          dtype=torch.float32, device=device)
+
+    def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None, workspace=None,
+             tile_stats=None, refresh_delta: float = float("inf")):
+        """One denoising step. With a workspace the query tiles run heaviest first; with
+        tile_stats the mask rows whose statistic moved by more than refresh_delta are cleared
+        (divergence refresh). The two options are separate entry points and do not combine."""
+        if tile_stats is not None:
+            if workspace is not None:
+                raise ValueError("workspace and tile_stats do not combine")
+            lite_attn_step_refresh(self.handle, q, k, v, out, mask, tile_stats, refresh_delta,
+                                   log_eps_t, step, stream)
+        elif workspace is None:
             lite_attn_step(self.handle, q, k, v, out, mask, log_eps_t, step, stream)
         else:
             lite_attn_step_scheduled(self.handle, q, k, v, out, mask, log_eps_t, step, workspace,

@@ -27,6 +27,7 @@ EXPORTS = (
     "lite_attn_mask_bytes",
     "lite_attn_mask_geometry",
     "lite_attn_step",
+    "lite_attn_step_refresh",
     "lite_attn_workspace_bytes",
     "lite_attn_step_scheduled",
     "lite_attn_reset_mask",
@@ -103,6 +104,9 @@ def _load() -> ctypes.CDLL:
     lib.lite_attn_mask_geometry.restype = ctypes.c_int
     lib.lite_attn_step.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32, vp]
     lib.lite_attn_step.restype = ctypes.c_int
+    lib.lite_attn_step_refresh.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_int32, vp]
+    lib.lite_attn_step_refresh.restype = ctypes.c_int
     lib.lite_attn_workspace_bytes.argtypes = [vp]
     lib.lite_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.lite_attn_step_scheduled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
@@ -280,6 +284,29 @@ def lite_attn_step(handle: Handle, q, k, v, out, mask, log_eps_t: float, step: i
                                ctypes.c_float(log_eps_t), ctypes.c_int32(step),
                                ctypes.c_void_p(st)),
            "lite_attn_step")
+
+
+def lite_attn_step_refresh(handle: Handle, q, k, v, out, mask, tile_stats, refresh_delta: float,
+                           log_eps_t: float, step: int, stream=None):
+    """lite_attn_step with divergence-triggered refresh; `tile_stats` is a float32 device tensor
+    of B*H*Tq references (NaN: none yet)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _check_qkvo(handle, t, name)
+    _check_mask(handle, mask)
+    torch = _torch()
+    if isinstance(tile_stats, torch.Tensor):
+        c = handle.cfg
+        if (tile_stats.dtype != torch.float32 or not tile_stats.is_contiguous() or
+                tile_stats.numel() < c.batch * c.heads * handle.tiles_q):
+            raise ValueError("tile_stats must be a contiguous float32 tensor of B*H*Tq elements")
+    dev = None if isinstance(q, int) else q.device
+    st = _stream_ptr(stream, dev)
+    _check(_lib.lite_attn_step_refresh(handle.ptr, _ptr(q, "q", dev), _ptr(k, "k", dev),
+                                       _ptr(v, "v", dev), _ptr(out, "out", dev),
+                                       _ptr(mask, "mask", dev), _ptr(tile_stats, "tile_stats", dev),
+                                       ctypes.c_float(refresh_delta), ctypes.c_float(log_eps_t),
+                                       ctypes.c_int32(step), ctypes.c_void_p(st)),
+           "lite_attn_step_refresh")
 
 
 def lite_attn_workspace_bytes(handle: Handle) -> int:

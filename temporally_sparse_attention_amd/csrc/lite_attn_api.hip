@@ -156,7 +156,8 @@ namespace {
 // Shared body of lite_attn_step and lite_attn_step_scheduled.
 int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, const void* v,
               void* out, uint32_t* mask, float log_eps_t, int32_t step, void* workspace,
-              bool scheduled, void* stream) {
+              bool scheduled, float* tile_stats, float refresh_delta, bool refresh,
+              void* stream) {
   try {
     if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL handle", who);
     if (std::isnan(log_eps_t) || log_eps_t > 0.f)
@@ -174,6 +175,11 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
       return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: out aliases an input", who);
     if (scheduled && (!workspace || !aligned(workspace, 256)))
       return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or not 256-byte aligned workspace", who);
+    if (refresh && (!tile_stats || !aligned(tile_stats, 4)))
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or misaligned tile_stats", who);
+    if (refresh && !(refresh_delta >= 0.f))
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: refresh_delta must be >= 0, got %g", who,
+                  (double)refresh_delta);
 
     const hipStream_t st = static_cast<hipStream_t>(stream);
     lite_attn::FwdParams p;
@@ -197,6 +203,8 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     p.descending = (c.order == LITE_ATTN_ORDER_ALT && (step & 1)) ? 1 : 0;
     p.dense_prefix = c.dense_prefix;
     p.perm = nullptr;
+    p.stats = refresh ? tile_stats : nullptr;
+    p.refresh_delta = refresh_delta;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;
       const hipError_t e = lite_attn::launch_plan(mask, n, h->W, h->Tk, workspace, st);
@@ -220,7 +228,15 @@ extern "C" {
 
 int lite_attn_step(lite_attn_t h, const void* q, const void* k, const void* v, void* out,
                    uint32_t* mask, float log_eps_t, int32_t step, void* stream) {
-  return step_impl("step", h, q, k, v, out, mask, log_eps_t, step, nullptr, false, stream);
+  return step_impl("step", h, q, k, v, out, mask, log_eps_t, step, nullptr, false, nullptr, 0.f,
+                   false, stream);
+}
+
+int lite_attn_step_refresh(lite_attn_t h, const void* q, const void* k, const void* v,
+                           void* out, uint32_t* mask, float* tile_stats, float refresh_delta,
+                           float log_eps_t, int32_t step, void* stream) {
+  return step_impl("step_refresh", h, q, k, v, out, mask, log_eps_t, step, nullptr, false,
+                   tile_stats, refresh_delta, true, stream);
 }
 
 size_t lite_attn_workspace_bytes(lite_attn_t h) {
@@ -232,7 +248,7 @@ int lite_attn_step_scheduled(lite_attn_t h, const void* q, const void* k, const 
                              void* out, uint32_t* mask, float log_eps_t, int32_t step,
                              void* workspace, void* stream) {
   return step_impl("step_scheduled", h, q, k, v, out, mask, log_eps_t, step, workspace, true,
-                   stream);
+                   nullptr, 0.f, false, stream);
 }
 
 int lite_attn_reset_mask(lite_attn_t h, uint32_t* mask, void* stream) {

@@ -26,6 +26,8 @@ struct FwdParams {
   int descending;     // traversal direction of this step
   int dense_prefix;   // tokens [0, dense_prefix) are exempt from flagging
   const uint32_t* perm;   // block -> query tile (B*H*Tq entries), or nullptr for the identity
+  float* stats;           // divergence-refresh references (B*H*Tq), or nullptr: no refresh
+  float refresh_delta;    // largest move of the statistic that keeps a mask row
 };
 
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);

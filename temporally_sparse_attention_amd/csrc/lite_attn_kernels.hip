@@ -135,6 +135,50 @@ __device__ void write_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* ke
   }
 }
 
+// Divergence-triggered refresh (LiteAttention, page 1 "Core Concept": the mask is updated only
+// when the attention pattern diverges significantly; "Architecture Overview": decisions carry
+// forward unless the attention distribution shifts). The statistic of the query tile is the
+// mean over its valid rows of the running row maximum m (raw scores; times `scale` gives
+// scaled units), taken after the tile loop. With no reference yet (NaN) it becomes the
+// reference; when it moves by more than `delta` (or the move is NaN) the reference is dropped
+// and the mask row is cleared instead of updated. Every thread calls this after the final
+// barrier of the tile loop; returns true when the row is to be cleared. Each wave's lanes 0..31
+// hold its 32 rows (lanes 32..63 hold copies), so wave sums are added in wave order: the
+// statistic is the same on every run.
+template <int NW>
+__device__ bool refresh_decision(float m_run, bool row_valid, int valid_rows, float scale,
+                                 float delta, float* stat_slot, float* s_part, int* s_clear) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float v = (lane < 32 && row_valid) ? m_run : 0.f;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) s_part[wave] = v;
+  __syncthreads();
+  if (tid == 0) {
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += s_part[w];
+    const float stat = total / (float)valid_rows * scale;
+    const float ref = *stat_slot;
+    int clear = 0;
+    if (ref != ref) {
+      *stat_slot = stat;
+    } else if (!(fabsf(stat - ref) <= delta)) {
+      *stat_slot = __builtin_nanf("");
+      clear = 1;
+    }
+    *s_clear = clear;
+  }
+  __syncthreads();
+  return *s_clear != 0;
+}
+
+// Clears the valid bits of a mask row (reserved bits stay as they are: zero).
+template <int NT>
+__device__ void clear_mask_row(uint32_t* mrow, int W, int Tk) {
+  for (int w = threadIdx.x; w < W; w += NT) mrow[w] &= ~valid_bits(w, Tk);
+}
+
 // ---------------------------------------------------------------------------------------
 // bf16 kernel: MFMA 32x32x16 bf16, software-pipelined across key tiles; K/V streamed straight
 // into LDS (double-buffered) with buffer loads; one workgroup barrier per visited tile.
@@ -454,8 +498,9 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   // no reference yet), moves the reference: exponentials then stay <= 256 and the common case
   // skips the accumulator rescale. `live` is false for the dummy tile after the last one.
   auto fold_max = [&](f32x16 (&s)[2], float nb, float tm, float mt, bool live) {
+    if (!live) return;   // the dummy tile after the last one holds stale scores
     m_run = nanmax(m_run, mt);
-    if (live && __ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
+    if (__ballot(m_ref == -INFINITY || tm > 8.f) != 0ull) {
       const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_run) * c2);
       const float shift = -m_run * c2 - nb;
       m_ref = m_run;
@@ -609,7 +654,15 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       }
   }
 
-  write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, row_exempt, exempt_cols);
+  bool clear = false;
+  if (p.stats) {
+    __shared__ float s_part[NW];
+    __shared__ int s_clear;
+    clear = refresh_decision<NW>(m_run, row_valid, min(BQ, N - i * BQ), p.scale,
+                                 p.refresh_delta, p.stats + tile, s_part, &s_clear);
+  }
+  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk);
+  else write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, row_exempt, exempt_cols);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -772,7 +825,15 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
       }
   }
   const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
-  write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, i * BQ < p.dense_prefix, exempt_cols);
+  bool clear = false;
+  if (p.stats) {
+    __shared__ float s_part[NW];
+    __shared__ int s_clear;
+    clear = refresh_decision<NW>(m_run, row_valid, min(BQ, N - i * BQ), p.scale,
+                                 p.refresh_delta, p.stats + tile, s_part, &s_clear);
+  }
+  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk);
+  else write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, i * BQ < p.dense_prefix, exempt_cols);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -128,6 +128,13 @@ def test_step_host_validation_makes_no_device_call():
     assert sc(ctypes.c_void_p(4096 + 128)) == binding.ERR_INVALID_ARG    # not 256-byte aligned
     assert lib.lite_attn_step_scheduled(h.ptr, p, p, p, ctypes.c_void_p(8192), ms,
                                         ctypes.c_float(0.5), 0, p, None) == binding.ERR_INVALID_ARG
+    rf = lambda stats, delta: lib.lite_attn_step_refresh(h.ptr, p, p, p, ctypes.c_void_p(8192), ms,
+                                                         stats, ctypes.c_float(delta),
+                                                         ctypes.c_float(-1.0), 0, None)
+    assert rf(None, 1.0) == binding.ERR_INVALID_ARG                     # no tile_stats
+    assert rf(ctypes.c_void_p(4098), 1.0) == binding.ERR_INVALID_ARG    # misaligned
+    assert rf(p, -1.0) == binding.ERR_INVALID_ARG                       # negative delta
+    assert rf(p, math.nan) == binding.ERR_INVALID_ARG                   # NaN delta
     n = 1 * 1 * 2   # B * H * Tq for N = 100, tile_q = 64
     assert tsa.lite_attn_workspace_bytes(h) >= 6 * n and tsa.lite_attn_workspace_bytes(h) % 256 == 0
     assert lib.lite_attn_workspace_bytes(None) == 0

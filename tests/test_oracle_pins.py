@@ -363,3 +363,84 @@ def test_in_step_skip_changes_output_by_at_most_the_flagged_mass():
                               in_step_skip=True, **kw)
     base = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=-math.inf, **kw)
     assert np.array_equal(same.out, base.out)
+
+
+# ------------------------------------------------------------------ divergence refresh
+def _brute_stat(q, k, skipped, tq, tk, scale, i):
+    """Mean over the valid rows of tile i of the largest scaled score over the columns of the
+    key tiles that are not skipped (pure Python)."""
+    n = len(q)
+    rows = range(i * tq, min(n, (i + 1) * tq))
+    vals = []
+    for r in rows:
+        best = -math.inf
+        for c in range(n):
+            if not skipped[c // tk]:
+                best = max(best, scale * sum(a * b for a, b in zip(q[r], k[c])))
+        vals.append(best)
+    return sum(vals) / len(vals)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_refresh_statistic_matches_brute_force_and_infinite_delta_changes_nothing(seed):
+    rng = np.random.default_rng(9000 + seed)
+    n = int(rng.integers(6, 30))
+    d = int(rng.integers(1, 4))
+    tq, tk = int(rng.choice([2, 4, 8])), int(rng.choice([2, 3, 4]))
+    q, k, v = _rand(rng, n, d, 2.0), _rand(rng, n, d, 2.0), _rand(rng, n, 2)
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    skipped = rng.random((tqn, tkn)) < 0.3
+    mask = bits_to_mask(skipped)[None, None]
+    kw = dict(tile_q=tq, tile_k=tk, softmax_scale=1.0, log_eps=-2.0, step=seed % 2, order="alt")
+    plain = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, **kw)
+    ref0 = np.full((1, 1, tqn), np.nan)
+    res = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, tile_stats=ref0,
+                             refresh_delta=math.inf, **kw)
+    for i in range(tqn):
+        want = _brute_stat(q, k, skipped[i].tolist(), tq, tk, 1.0, i)
+        assert res.stats[0, 0, i] == pytest.approx(want, rel=1e-12, abs=1e-12) or (
+            math.isinf(want) and res.stats[0, 0, i] == want)
+    # a first step only records the reference; an infinite delta never refreshes
+    np.testing.assert_array_equal(res.stats_next, res.stats)
+    assert np.array_equal(res.mask_next, plain.mask_next) and not res.refreshed.any()
+    np.testing.assert_array_equal(np.nan_to_num(res.out), np.nan_to_num(plain.out))
+    again = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask,
+                               tile_stats=res.stats_next + 1e9, refresh_delta=math.inf, **kw)
+    assert np.array_equal(again.mask_next, plain.mask_next)
+    np.testing.assert_array_equal(again.stats_next, res.stats_next + 1e9)
+
+
+def test_refresh_clears_a_row_when_the_attention_moves_into_skipped_tiles():
+    """Local attention (query r looks at key r); step 1 flags far tiles; at step 2 the keys are
+    rolled so the best keys of every row lie in tiles that step 1 flagged: the row maxima over
+    the computed tiles fall, the statistic moves by more than delta, and the rows are cleared
+    (and the reference dropped); with a large delta nothing is cleared."""
+    n, tq, tk = 32, 8, 8
+    x = np.arange(n)
+    q = np.stack([np.cos(2 * np.pi * x / n), np.sin(2 * np.pi * x / n)], axis=1) * 4.0
+    k = q.copy()
+    v = np.eye(n)[:, :3]
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    kw = dict(tile_q=tq, tile_k=tk, softmax_scale=1.0, order="asc")
+    stats = np.full((1, 1, tqn), np.nan)
+    mask = empty_mask(1, 1, n, tq, tk)
+    r0 = lite_attn_step_ref(_one_head(q), _one_head(k), _one_head(v), mask, log_eps=-8.0, step=0,
+                            tile_stats=stats, refresh_delta=2.0, **kw)
+    assert not r0.refreshed.any() and not np.isnan(r0.stats_next).any()
+    flagged = mask_to_bits(r0.mask_next, tkn)[0, 0]
+    assert flagged.any()
+    k2 = np.roll(k, n // 2, axis=0)        # every row's best keys move half the circle away
+    r1 = lite_attn_step_ref(_one_head(q), _one_head(k2), _one_head(v), r0.mask_next, log_eps=-8.0,
+                            step=1, tile_stats=r0.stats_next, refresh_delta=2.0, **kw)
+    moved = np.abs(r1.stats - r0.stats_next)[0, 0]
+    for i in range(tqn):
+        if moved[i] > 2.0:
+            assert r1.refreshed[0, 0, i] and not r1.mask_next[0, 0, i].any()
+            assert math.isnan(r1.stats_next[0, 0, i])
+        else:
+            assert not r1.refreshed[0, 0, i]
+    assert r1.refreshed.any()
+    keep = lite_attn_step_ref(_one_head(q), _one_head(k2), _one_head(v), r0.mask_next, log_eps=-8.0,
+                              step=1, tile_stats=r0.stats_next, refresh_delta=1e6, **kw)
+    assert not keep.refreshed.any()
+    assert np.array_equal(keep.mask_next, keep.mask_next | r0.mask_next)   # bits only grow
