@@ -65,6 +65,10 @@ def parse_args():
     ap.add_argument("--refresh-delta", type=float, default=None,
                     help="use lite_attn_step_refresh with this divergence budget (mask rows whose "
                          "statistic moves by more are cleared)")
+    ap.add_argument("--calibrate", default=None, metavar="LO,HI",
+                    help="derive the log_eps schedule with calibrate_schedule (untimed, before the "
+                         "warmup) from output-error budgets rising linearly from LO to HI (max "
+                         "|out - dense|), and time that schedule instead of the workload's")
     ap.add_argument("--in-step-skip", action="store_true",
                     help="enable the in-step-skip option (tiles flagged in a step also leave that "
                          "step's output; their exponentials and PV are not computed)")
@@ -241,6 +245,19 @@ def main():
     out = torch.empty_like(qs[0])
     mask = att.new_mask(dev)
     stream = torch.cuda.current_stream(dev)
+    log_eps = list(cfg.log_eps)
+    calibration = None
+    if args.calibrate:
+        lo, hi = (float(x) for x in args.calibrate.split(","))
+        n_st = cfg.steps
+        budgets = [lo + (hi - lo) * t / max(1, n_st - 1) for t in range(n_st)]
+        log(f"[bench] calibrating log_eps for budgets {lo} .. {hi}")
+        res = tsa.calibrate_schedule(tsa.LiteAttentionRunner(att, dev),
+                                     lambda t: (qs[t], ks[t], v), n_st, budgets)
+        log_eps = list(res.log_eps)
+        calibration = res.as_dict()
+        calibration["log_eps"] = [None if math.isinf(x) else x for x in res.log_eps]
+        log(f"[bench] calibrated log_eps {log_eps}")
     workspace = att.new_workspace(dev) if args.schedule else None
     refresh = args.refresh_delta is not None
     if refresh and args.schedule:
@@ -257,10 +274,10 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         if refresh:
-            att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, tile_stats=stats,
+            att.step(qs[t], ks[t], v, out, mask, log_eps[t], t, tile_stats=stats,
                      refresh_delta=args.refresh_delta)
         else:
-            att.step(qs[t], ks[t], v, out, mask, cfg.log_eps[t], t, workspace=workspace)
+            att.step(qs[t], ks[t], v, out, mask, log_eps[t], t, workspace=workspace)
         if ev is not None:
             ev[1].record(stream)
 
@@ -293,10 +310,10 @@ def main():
         if k_idx >= warmup:
             f, kvb, sfrac = computed_work(mask2, cfg, tiles_q, tiles_k)
         if refresh:
-            att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t, tile_stats=stats2,
+            att.step(qs[t], ks[t], v, out, mask2, log_eps[t], t, tile_stats=stats2,
                      refresh_delta=args.refresh_delta)
         else:
-            att.step(qs[t], ks[t], v, out, mask2, cfg.log_eps[t], t)
+            att.step(qs[t], ks[t], v, out, mask2, log_eps[t], t)
         if k_idx >= warmup:
             if args.in_step_skip:
                 # tiles flagged during this step were scored (QK) but got no PV product
@@ -353,6 +370,7 @@ def main():
             "dense_prefix": cfg.dense_prefix, "parallelism": "single GPU",
             "in_step_skip": bool(args.in_step_skip), "schedule": bool(args.schedule),
             "refresh_delta": args.refresh_delta,
+            "log_eps": [None if math.isinf(x) else x for x in log_eps],   # None: -inf
         },
         "skipped_tile_fraction": round(sum(skipped) / len(skipped), 4),
         "dense_step_tflops_equiv_per_step": None,
@@ -371,6 +389,8 @@ def main():
     if a is not None:
         result["time_fit"] = {"t_dense_ms": round(a, 3), "t0_ms": round(b0, 3),
                               "r2": None if r2 is None else round(r2, 4)}
+    if calibration is not None:
+        result["calibration"] = calibration
     if args.per_step:
         result["per_step"] = [
             {"t": (warmup + s) % cfg.steps, "kernel_ms": round(kernel_ms[s], 4),

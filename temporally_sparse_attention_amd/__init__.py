@@ -29,7 +29,12 @@ from .binding import (  # noqa: F401
     lite_attn_workspace_bytes,
     make_config,
 )
-from .schedule import ErrorBudgetSchedule  # noqa: F401
+from .schedule import (  # noqa: F401
+    CalibrationResult,
+    ErrorBudgetSchedule,
+    LiteAttentionRunner,
+    calibrate_schedule,
+)
 
 
 class LiteAttention:
