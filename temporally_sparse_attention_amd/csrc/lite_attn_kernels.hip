@@ -283,6 +283,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_v1[G::V_BYTES];
   __shared__ uint16_t s_list[kMaxTilesK];
   __shared__ uint32_t s_keep[kMaxWords];
+  __shared__ uint64_t s_wkeep[NW][kMaxTilesK / 64];   // per-wave keep votes by list position
   __shared__ int s_count;
 
   const int tid = threadIdx.x;
@@ -528,6 +529,19 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       if (lane == 0) atomicOr(&s_keep[j >> 5], 1u << (j & 31));
     }
   };
+  // Without in-step skip nobody needs a tile's votes before the end, so each wave collects its
+  // keep votes as bits of a scalar register indexed by list position, and stores the register
+  // to LDS every 64 positions; the bits are combined into the keep bitset after the loop.
+  uint64_t kmask = 0ull;
+  auto vote_batched = [&](int n, float mt, float mp) {
+    const float diff = (mt - mp) * p.scale;
+    const bool below = !row_valid || diff < p.log_eps;
+    if (__ballot(!below) != 0ull) kmask |= 1ull << (n & 63);
+    if ((n & 63) == 63 || n == cnt - 1) {
+      if (lane == 0) s_wkeep[wave][n >> 6] = kmask;
+      kmask = 0ull;
+    }
+  };
   const bool row_exempt = i * BQ < p.dense_prefix;
   const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
 
@@ -575,7 +589,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       qk_mfma(kst, tn);
       l_run += exp_pack(tc, pb);
       phase_a_sched();
-      if constexpr (!INSTEP) vote(j, mt, mp);
+      if constexpr (!INSTEP) vote_batched(n, mt, mp);
       if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
       // phase B
       nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
@@ -637,6 +651,19 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     }
   }
   __syncthreads();
+  if constexpr (!INSTEP) {
+    // a visited tile is kept when any wave voted keep at its list position
+    for (int pos = tid; pos < cnt; pos += NT) {
+      uint64_t any = 0ull;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) any |= s_wkeep[w][pos >> 6];
+      if ((any >> (pos & 63)) & 1ull) {
+        const int jj = s_list[pos];
+        atomicOr(&s_keep[jj >> 5], 1u << (jj & 31));
+      }
+    }
+    __syncthreads();
+  }
 
   // Epilogue: normalise and store this wave's rows.
   const float l_tot = halves_sum(l_run);
