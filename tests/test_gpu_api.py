@@ -180,3 +180,36 @@ def test_binding_rejects_bad_tensors():
         att.step(q, q, q, torch.empty_like(q), mask, 0.5, 0)
     with pytest.raises(tsa.LiteAttnError):
         att.step(q, q, q, q, mask, -1.0, 0)   # out aliases q
+
+
+def test_largest_supported_length():
+    """N = 131072 (2048 key tiles, the visiting-list capacity; 64 mask words per row), with a
+    random mask that leaves about half the tiles; sampled query tiles against the oracle, and
+    the whole output finite."""
+    dev = device()
+    n, D = 131072, 128
+    tq, tk, w = mask_geometry(n, 128, 64)
+    assert tk == 2048 and w == 64
+    rng = np.random.default_rng(131072)
+    bits = rng.random((1, 1, tq, tk)) < 0.5
+    bits[0, 0, :, 0] = False
+    mask_np = bits_to_mask(bits)
+    q, k, v = _rand_inputs(1, 1, n, D, torch.bfloat16, 7, 1.0)
+    att = tsa.LiteAttention(1, 1, n, D, tile_q=128, dtype="bf16", softmax_scale=1.0 / 11.3)
+    out = torch.empty((1, 1, n, D), dtype=torch.bfloat16, device=dev)
+    mask = to_mask_tensor(mask_np, dev)
+    att.step(q.to(dev), k.to(dev), v.to(dev), out, mask, -0.3, 1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    rows = [(0, 0, i) for i in (0, 1, 511, tq - 1)]
+    ref = lite_attn_step_ref(q, k, v, mask_np, tile_q=128, tile_k=64, softmax_scale=1.0 / 11.3,
+                             log_eps=-0.3, step=1, order="alt", rows=rows)
+    got = out.double().cpu().numpy()
+    gbits = mask_to_bits(from_mask_tensor(mask), tk)
+    rbits = mask_to_bits(ref.mask_next, tk)
+    c = Comparison()
+    for (_, _, i) in rows:
+        r0, r1 = i * 128, min(n, (i + 1) * 128)
+        c.add_out(got[0, 0, r0:r1], ref.out[0, 0, r0:r1])
+        c.add_mask(gbits[0, 0, i], rbits[0, 0, i], ref.margins[0, 0, i], bits[0, 0, i])
+    c.check("N=131072")
