@@ -338,7 +338,10 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": traffic_per_launch(khash, cfg.name),
+        # counters were taken on the plain step (no option) of the default schedule
+        "traffic": (traffic_per_launch(khash, cfg.name)
+                    if not (args.in_step_skip or args.schedule or refresh or args.calibrate)
+                    else None),
         "kernel": f"lite_attn_fwd_{dt_name} (D={cfg.head_dim}, tile {cfg.tile_q}x{cfg.tile_k})",
         "kernel_ms_mean": round(mean_ms, 4),
         "flops_per_launch_mean": sum(flops) / len(flops),
