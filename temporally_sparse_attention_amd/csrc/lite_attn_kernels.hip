@@ -281,7 +281,7 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_k1[G::K_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char s_v0[G::V_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char s_v1[G::V_BYTES];
-  __shared__ uint16_t s_list[kMaxTilesK];
+  __shared__ uint16_t s_list[kMaxTilesK + 8];   // +8: the loop reads a few entries ahead
   __shared__ uint32_t s_keep[kMaxWords];
   __shared__ uint64_t s_wkeep[NW][kMaxTilesK / 64];   // per-wave keep votes by list position
   __shared__ int s_count;
@@ -474,6 +474,20 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     tm = halves_max(nanmax(tm0, tm1));
     return (tm - nb) * inv_c2;
   };
+  // The ragged last key tile, after scale_max: keys >= N get -inf and the maxima are taken
+  // again over the remaining keys.
+  auto ragged_fix = [&](int j, f32x16 (&s)[2], float nb, float& tm) {
+    mask_ragged(j, s);
+    float tm0 = nanmax(nanmax(s[0][0], s[1][0]), s[0][2]);
+    float tm1 = nanmax(nanmax(s[0][1], s[1][1]), s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 16; r += 2) {
+      tm0 = nanmax(nanmax(tm0, s[0][r]), s[1][r]);
+      if (r + 1 < 16) tm1 = nanmax(nanmax(tm1, s[0][r + 1]), s[1][r + 1]);
+    }
+    tm = halves_max(nanmax(tm0, tm1));
+    return (tm - nb) * inv_c2;
+  };
   // P as bf16 B operands (16-key step kc: registers 8(kc%2) .. +7 of t[kc/2]) and the row sum
   // over the same rounded weights (v_dot2 with ones, two partial sums).
   auto exp_pack = [&](const f32x16 (&t)[2], bf16x8 (&pb)[4]) {
@@ -568,6 +582,10 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   auto iteration = [&](int n, int j, int j1, int j2, f32x16 (&tc)[2], f32x16 (&tn)[2],
                        float& mt, float& mp, const unsigned char* kst, unsigned char* kfree,
                        const unsigned char* vst, unsigned char* vfree) {
+    // Tile n's vote needs only its row maximum and the running maximum before it. It is cast
+    // here, ahead of the pipelined body, so that its branch (the store of the vote register
+    // every 64 positions) does not split the body either.
+    if constexpr (!INSTEP) vote_batched(n, mt, mp);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads have landed
     __syncthreads();                                      // everyone's; iteration n-1 is done
     if (n + 2 < cnt) issue_k(j2, kfree);
@@ -589,13 +607,17 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
       qk_mfma(kst, tn);
       l_run += exp_pack(tc, pb);
       phase_a_sched();
-      if constexpr (!INSTEP) vote_batched(n, mt, mp);
-      if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
       // phase B
       nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
       pv_mfma(vst, pb);
       mt1 = scale_max(tn, nb, tm);
       phase_b_sched();
+      // The ragged last key tile is fixed up after phase B rather than masked between the two
+      // phases: a branch there would split the body into two basic blocks, and the compiler
+      // would then move tile n's exponentials out of phase A. The empty asm keeps the maxima
+      // computed in phase B.
+      asm volatile("" : "+v"(mt1), "+v"(tm));
+      if (live && (j1 + 1) * BK > N) mt1 = ragged_fix(j1, tn, nb, tm);
     } else {
       qk_mfma(kst, tn);
       __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
@@ -639,15 +661,20 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   }
   // Main loop, unrolled by two so that every stage is named statically. The list entries two
   // positions ahead are read early so that tile indices are in scalar registers.
+  // List entries are read into vector registers one iteration before they are needed, so
+  // that the LDS latency of the read is hidden (entries past cnt are read but never used).
+  int jv3 = s_list[3];
   for (int n = 0; n < cnt; n += 2) {
-    int j3 = n + 3 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 3]) : 0;
+    const int jv4 = s_list[n + 4];
     iteration(n, j0, j1, j2, ta, tb, mt, mp, s_k1, s_k0, s_v0, s_v1);
+    const int j3 = __builtin_amdgcn_readfirstlane(jv3);
     if (n + 1 < cnt) {
-      const int j4 = n + 4 < cnt ? __builtin_amdgcn_readfirstlane(s_list[n + 4]) : 0;
+      const int jv5 = s_list[n + 5];
       iteration(n + 1, j1, j2, j3, tb, ta, mt, mp, s_k0, s_k1, s_v1, s_v0);
       j0 = j2;
       j1 = j3;
-      j2 = j4;
+      j2 = __builtin_amdgcn_readfirstlane(jv4);
+      jv3 = jv5;
     }
   }
   __syncthreads();
