@@ -26,6 +26,15 @@
  * - A handle holds only the validated configuration; it owns no device memory. Steps on the
  *   same handle may run concurrently on different streams when their out and mask buffers
  *   differ.
+ * - bf16 steps run as persistent launches: a grid of as many workgroups as the device holds
+ *   at once takes query tiles from a tile queue, a pair of uint32 in the library's static
+ *   device memory. Each (device, stream) pair is given one of 64 queues per device on first
+ *   use and keeps it; launches on one stream run one after another, and each launch leaves
+ *   its queue at zero when it ends. A step falls back to one workgroup per query tile (same
+ *   results, no queue) when all 64 queues of the device are taken, for the per-thread
+ *   default stream, and when the stream belongs to a device other than the current one.
+ *   A stream must not be destroyed while its steps are still running (its handle value
+ *   could then be reused by a new stream while the queue is in use).
  */
 #ifndef LITE_ATTN_H
 #define LITE_ATTN_H

@@ -1,5 +1,6 @@
 // C ABI of the LiteAttention step library (declared in include/lite_attn.h): argument
-// validation, error reporting and kernel dispatch. No device memory is allocated here.
+// validation, error reporting and kernel dispatch. No device memory is allocated here (the
+// persistent launches' tile queues are static device memory of the library).
 
 #include <hip/hip_runtime.h>
 
@@ -7,8 +8,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
+#include <utility>
 
 #include "lite_attn.h"
 #include "lite_attn_internal.h"
@@ -38,6 +42,55 @@ int fail(int code, const char* fmt, ...) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile queue of a stream for persistent launches. Each (device, stream) pair gets one of the
+// device's kQueueSlots queues for the life of the process; launches on one stream run one after
+// another, so a queue is never used by two launches at once. Returns nullptr (the launch then
+// takes one workgroup per tile) when the stream belongs to another device than the current
+// one, for the per-thread default stream (one handle value, many streams), or when every queue
+// of the device is taken.
+struct QueueTable {
+  std::mutex mu;
+  std::map<std::pair<int, uintptr_t>, int> slot;
+  std::map<int, int> used;
+  std::map<int, int> cus;
+};
+
+QueueTable& queue_table() {
+  static QueueTable* t = new QueueTable;   // never destroyed: usable during static teardown
+  return *t;
+}
+
+uint32_t* stream_queue(hipStream_t st, int* n_cu) {
+  *n_cu = 0;
+  if (st == hipStreamPerThread) return nullptr;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (st != nullptr) {
+    int dev = -1;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess || dev != cur) return nullptr;
+  }
+  QueueTable& t = queue_table();
+  std::lock_guard<std::mutex> lock(t.mu);
+  auto c = t.cus.find(cur);
+  if (c == t.cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, cur) != hipSuccess)
+      return nullptr;
+    c = t.cus.emplace(cur, n).first;
+  }
+  const auto key = std::make_pair(cur, reinterpret_cast<uintptr_t>(st));
+  auto it = t.slot.find(key);
+  if (it == t.slot.end()) {
+    int& used = t.used[cur];
+    if (used >= lite_attn::kQueueSlots) return nullptr;
+    it = t.slot.emplace(key, used++).first;
+  }
+  uint32_t* q = nullptr;
+  if (lite_attn::tile_queue_address(it->second, &q) != hipSuccess) return nullptr;
+  *n_cu = c->second;
+  return q;
+}
 
 }  // namespace
 
@@ -205,6 +258,8 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     p.perm = nullptr;
     p.stats = refresh ? tile_stats : nullptr;
     p.refresh_delta = refresh_delta;
+    p.queue = h->cfg.dtype == LITE_ATTN_BF16 ? stream_queue(st, &p.n_cu) : nullptr;
+    if (!p.queue) p.n_cu = 0;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;
       const hipError_t e = lite_attn::launch_plan(mask, n, h->W, h->Tk, workspace, st);

@@ -9,6 +9,7 @@ namespace lite_attn {
 constexpr int kTileK = 64;          // keys per tile (two 32-key MFMA blocks)
 constexpr int kMaxTilesK = 2048;    // visiting list capacity per query tile (LDS)
 constexpr int kMaxWords = kMaxTilesK / 32;
+constexpr int kQueueSlots = 64;     // tile queues per device for persistent launches
 
 // Everything one forward launch needs. Strides are in elements.
 struct FwdParams {
@@ -28,6 +29,11 @@ struct FwdParams {
   const uint32_t* perm;   // block -> query tile (B*H*Tq entries), or nullptr for the identity
   float* stats;           // divergence-refresh references (B*H*Tq), or nullptr: no refresh
   float refresh_delta;    // largest move of the statistic that keeps a mask row
+  // Persistent launch: a tile queue (two uint32: next tile, finished workgroups; both zero
+  // between launches) and the device's compute-unit count, which sizes the grid. With
+  // queue == nullptr every workgroup takes the one tile of its block index.
+  uint32_t* queue;
+  int n_cu;
 };
 
 using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
@@ -37,6 +43,9 @@ using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
 FwdLauncher get_fwd_launcher(int dtype, int head_dim, int tile_q, bool in_step_skip);
 
 hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream);
+
+// Device address of tile queue `slot` (0 <= slot < kQueueSlots) on the current device.
+hipError_t tile_queue_address(int slot, uint32_t** out);
 
 // Heaviest-first schedule of the query tiles of a mask: the workspace receives the block ->
 // tile permutation (n_tiles uint32 at offset 0) and scratch bucket bytes after it.

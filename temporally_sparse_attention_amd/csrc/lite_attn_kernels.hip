@@ -34,6 +34,11 @@
 #include "lite_attn_internal.h"
 
 namespace lite_attn {
+
+// Tile queues of persistent launches, kQueueSlots pairs (next tile, finished workgroups) per
+// device. Zero at load; every persistent launch leaves its pair at zero when it ends.
+__device__ uint32_t g_tile_queues[2 * kQueueSlots];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -267,9 +272,20 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 }
 #endif
 
+// The launch parameters as the kernel received them, read through scalar loads.
+typedef const FwdParams __attribute__((address_space(4))) ArgParams;
+
+// One query tile. Called by the kernel below for every tile it takes; kept out of line so that
+// the tile's register allocation does not carry the kernel's loop state. `args` is the address
+// of the kernel's argument segment (the FwdParams), `w_in` the tile's position (in the schedule
+// when there is one).
 template <int D, int NW, bool INSTEP>
-__global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
+__device__ __attribute__((noinline)) void bf16_tile(uint64_t args, uint32_t w_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t a_lo = __builtin_amdgcn_readfirstlane((uint32_t)args);
+  const uint32_t a_hi = __builtin_amdgcn_readfirstlane((uint32_t)(args >> 32));
+  ArgParams& p = *(ArgParams*)(((uint64_t)a_hi << 32) | a_lo);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(w_in);
   using G = Bf16TileGeom<D>;
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
@@ -292,12 +308,8 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Block index = logical tile (b * H + h) * Tq + i, unless a schedule permutes them.
-  // Workgroups are dispatched to the 8 XCDs round-robin, so each XCD receives every 8th query
-  // tile of every head: an even share of every head and of every region of a head, which keeps
-  // the XCDs balanced when skip densities differ, while all XCDs stream the same head's K/V
-  // (it stays in the MALL).
-  const uint32_t tile = p.perm ? p.perm[blockIdx.x] : blockIdx.x;
+  // Position = logical tile (b * H + h) * Tq + i, unless a schedule permutes them.
+  const uint32_t tile = p.perm ? p.perm[w] : w;
   const int i = (int)(tile % (uint32_t)p.Tq);
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
@@ -720,6 +732,43 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// bf16 attention step. Without a queue, workgroup b takes the tile at position b. With one, the
+// grid is sized to the workgroups the device holds at once and each workgroup takes positions
+// from the queue until none is left: a workgroup that finishes a short tile starts the next
+// one at once. (With one workgroup per tile, the dispatcher deals the workgroups of an XCD to
+// its shader engines in a fixed rotation, so when tile lengths differ, as they do once tiles
+// are skipped, free slots wait for their turn.) The last workgroup to finish puts the queue
+// back to zero for the next launch on its stream.
+template <int D, int NW, bool INSTEP>
+__global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
+  const uint64_t args = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+  if (p.queue == nullptr) {
+    bf16_tile<D, NW, INSTEP>(args, blockIdx.x);
+    return;
+  }
+  __shared__ uint32_t s_next;
+  const uint32_t n_tiles = (uint32_t)(p.B * p.H * p.Tq);
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_next = __hip_atomic_fetch_add(&p.queue[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t w = s_next;
+    if (w >= n_tiles) break;   // the same value in every thread
+    bf16_tile<D, NW, INSTEP>(args, w);
+    __syncthreads();           // LDS and s_next are reused by the next tile
+  }
+  // Every workgroup has taken its last position before it counts itself finished, so the last
+  // one to finish can reset the queue.
+  if (threadIdx.x == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(&p.queue[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1) {
+      __hip_atomic_store(&p.queue[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.queue[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // fp32 kernel: MFMA 32x32x2 f32, single-buffered (the fp32 workload is small).
 // ---------------------------------------------------------------------------------------
@@ -990,7 +1039,21 @@ __global__ void __launch_bounds__(256) mask_popcount(const uint32_t* mask, uint3
 // errors left behind by other HIP users in the process).
 template <int D, int NW, bool INSTEP>
 hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.Tq);
+  const unsigned tiles = (unsigned)((int64_t)p.B * p.H * p.Tq);
+  unsigned grid = tiles;
+  if (p.queue != nullptr) {
+    // workgroups per compute unit at this kernel's register and LDS use (two)
+    static const int per_cu = [] {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &n, reinterpret_cast<const void*>(&lite_attn_fwd_bf16<D, NW, INSTEP>), NW * 64,
+              0) != hipSuccess)
+        n = 0;
+      return n;
+    }();
+    const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * (p.n_cu > 0 ? p.n_cu : 1);
+    if (resident < (int64_t)grid) grid = (unsigned)resident;
+  }
   FwdParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_bf16<D, NW, INSTEP>),
@@ -1036,6 +1099,16 @@ hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t strea
   void* args[] = {&mask, &words};
   return hipLaunchKernel(reinterpret_cast<const void*>(&mask_fill_zero), dim3((unsigned)blocks),
                          dim3(256), args, 0, stream);
+}
+
+hipError_t tile_queue_address(int slot, uint32_t** out) {
+  *out = nullptr;
+  if (slot < 0 || slot >= kQueueSlots) return hipErrorInvalidValue;
+  void* base = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&base, HIP_SYMBOL(g_tile_queues));
+  if (e != hipSuccess) return e;
+  *out = static_cast<uint32_t*>(base) + 2 * slot;
+  return hipSuccess;
 }
 
 size_t plan_workspace_bytes(int64_t n_tiles) {
