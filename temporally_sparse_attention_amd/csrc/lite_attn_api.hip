@@ -258,7 +258,7 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     p.perm = nullptr;
     p.stats = refresh ? tile_stats : nullptr;
     p.refresh_delta = refresh_delta;
-    p.queue = h->cfg.dtype == LITE_ATTN_BF16 ? stream_queue(st, &p.n_cu) : nullptr;
+    p.queue = c.dtype == LITE_ATTN_BF16 ? stream_queue(st, &p.n_cu) : nullptr;   // persistent
     if (!p.queue) p.n_cu = 0;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;

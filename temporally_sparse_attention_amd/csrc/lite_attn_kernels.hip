@@ -279,9 +279,10 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 typedef const FwdParams __attribute__((address_space(4))) ArgParams;
 
 // One query tile. Called by the kernel below for every tile it takes; kept out of line so that
-// the tile's register allocation does not carry the kernel's loop state. `args` is the address
-// of the kernel's argument segment (the FwdParams), `w_in` the tile's position (in the schedule
-// when there is one).
+// the tile's register allocation does not carry the kernel's loop state (inlined into the loop,
+// the tile needed more scalar registers than there are, and the spills undid its instruction
+// schedule). `args` is the address of the kernel's argument segment (the FwdParams), `w_in` the
+// tile's position (in the schedule when there is one).
 template <int D, int NW, bool INSTEP>
 __device__ __attribute__((noinline)) void bf16_tile(uint64_t args, uint32_t w_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -624,6 +625,11 @@ __device__ __attribute__((noinline)) void bf16_tile(uint64_t args, uint32_t w_in
       qk_mfma(kst, tn);
       l_run += exp_pack(tc, pb);
       phase_a_sched();
+      // In-step skip masks the ragged tile between the phases: it has more live registers, and
+      // in the whole-body form below (tile n's exponentials kept in phase A) it spills.
+      if constexpr (INSTEP) {
+        if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
+      }
       // phase B
       nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
       pv_mfma(vst, pb);
@@ -633,8 +639,10 @@ __device__ __attribute__((noinline)) void bf16_tile(uint64_t args, uint32_t w_in
       // phases: a branch there would split the body into two basic blocks, and the compiler
       // would then move tile n's exponentials out of phase A. The empty asm keeps the maxima
       // computed in phase B.
-      asm volatile("" : "+v"(mt1), "+v"(tm));
-      if (live && (j1 + 1) * BK > N) mt1 = ragged_fix(j1, tn, nb, tm);
+      if constexpr (!INSTEP) {
+        asm volatile("" : "+v"(mt1), "+v"(tm));
+        if (live && (j1 + 1) * BK > N) mt1 = ragged_fix(j1, tn, nb, tm);
+      }
     } else {
       qk_mfma(kst, tn);
       __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);
