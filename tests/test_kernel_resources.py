@@ -1,0 +1,52 @@
+"""Resource use of the attention kernels as the compiler reports it (CPU: hipcc cross-compiles
+gfx950). The bf16 kernels are tuned for two workgroups per compute unit with no register
+spills: a spill inside the tile loop halves the rate, and more LDS or registers halve the
+occupancy. This test pins those properties so that a change that breaks them fails here rather
+than only on the device."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "temporally_sparse_attention_amd", "csrc")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _remarks(tmp_path):
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-c",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           os.path.join(CSRC, "lite_attn_kernels.hip"), "-o", str(tmp_path / "k.o"),
+           "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    kernels, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = {}
+            continue
+        m = re.search(r"remark:(.*)\[-Rpass", line)
+        if cur and m:
+            text = re.sub(r"^.*?:\d+:\d+:", "", m.group(1))   # a leading source location, if any
+            m2 = re.match(r"\s*([A-Za-z ]+?)(?: \[[^\]]+\])?: (\d+)\s*$", text)
+            if m2:
+                kernels[cur][m2.group(1).strip()] = int(m2.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_bf16_kernels_fit_two_workgroups_per_cu_without_spills(tmp_path):
+    k = _remarks(tmp_path)
+    bf16 = {n: v for n, v in k.items() if "lite_attn_fwd_bf16" in n}
+    assert len(bf16) == 8, sorted(k)            # D 64/128 x tile_q 64/128 x in-step skip
+    for name, v in bf16.items():
+        assert v.get("VGPRs Spill", -1) == 0, (name, v)
+        assert v.get("Occupancy", 0) >= 1, (name, v)
+        assert v.get("LDS Size", 1 << 30) <= 80 * 1024, (name, v)   # two per 160 KiB CU
+        if "ILi4E" in name:                      # tile_q 128: four waves, two workgroups per CU
+            assert v.get("Occupancy", 0) >= 2, (name, v)
