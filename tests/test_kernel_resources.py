@@ -50,3 +50,31 @@ def test_bf16_kernels_fit_two_workgroups_per_cu_without_spills(tmp_path):
         assert v.get("LDS Size", 1 << 30) <= 80 * 1024, (name, v)   # two per 160 KiB CU
         if "ILi4E" in name:                      # tile_q 128: four waves, two workgroups per CU
             assert v.get("Occupancy", 0) >= 2, (name, v)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_tile_loop_has_no_scratch_traffic(tmp_path):
+    """The tile itself is an out-of-line function, whose spills the kernel's remarks do not
+    show: read its assembly. The tile loop is the stretch between two workgroup barriers that
+    holds the most MFMAs; for tile_q 128 it must not touch scratch memory (the saves of
+    callee-saved registers at the function's entry and exit lie outside it)."""
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+           os.path.join(CSRC, "lite_attn_kernels.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    asm = out.read_text()
+    found = 0
+    for m in re.finditer(r"^(_ZN\w*bf16_tile\w*):", asm, re.M):
+        body = asm[m.start():asm.index(".Lfunc_end", m.start())].split("\n")
+        bars = [i for i, l in enumerate(body) if "s_barrier" in l]
+        assert len(bars) >= 2, m.group(1)
+        spans = [(sum("v_mfma" in l for l in body[a:b]), a, b) for a, b in zip(bars, bars[1:])]
+        mfmas, a, b = max(spans)
+        scratch = sum("scratch_" in l for l in body[a:b])
+        found += 1
+        limit = 0 if "ILi4E" in m.group(1) else 8
+        assert scratch <= limit, (m.group(1), scratch)
+    assert found == 8
