@@ -54,6 +54,7 @@ struct QueueTable {
   std::map<std::pair<int, uintptr_t>, int> slot;
   std::map<int, int> used;
   std::map<int, int> cus;
+  std::map<int, uint32_t*> base;   // queue 0 of each device
 };
 
 QueueTable& queue_table() {
@@ -86,10 +87,14 @@ uint32_t* stream_queue(hipStream_t st, int* n_cu) {
     if (used >= lite_attn::kQueueSlots) return nullptr;
     it = t.slot.emplace(key, used++).first;
   }
-  uint32_t* q = nullptr;
-  if (lite_attn::tile_queue_address(it->second, &q) != hipSuccess) return nullptr;
+  auto b = t.base.find(cur);
+  if (b == t.base.end()) {
+    uint32_t* q0 = nullptr;
+    if (lite_attn::tile_queue_address(0, &q0) != hipSuccess) return nullptr;
+    b = t.base.emplace(cur, q0).first;
+  }
   *n_cu = c->second;
-  return q;
+  return b->second + 2 * it->second;
 }
 
 }  // namespace

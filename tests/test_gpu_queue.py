@@ -85,3 +85,28 @@ def test_back_to_back_launches_of_different_sizes():
     for (gb, gs) in res:
         assert torch.equal(gb[0], rb[0]) and torch.equal(gb[1], rb[1])
         assert torch.equal(gs[0], rs[0]) and torch.equal(gs[1], rs[1])
+
+
+def test_graph_replays_match_eager():
+    """A step captured in a HIP graph (torch.cuda.graph) replays the persistent launch with the
+    queue of the capture stream; the queue is back at zero after every replay, so each replay
+    (with eager work on the GPU in between) gives the eager result."""
+    B, H, N, D = 1, 4, 6000, 128
+    att = tsa.LiteAttention(B, H, N, D, tile_q=128, dtype="bf16", softmax_scale=1 / 11.3)
+    q, k, v, mask0 = _case(B, H, N, D, 21)
+    ro, rm = _run(att, q, k, v, mask0, -3.0, 1)
+    torch.cuda.synchronize()
+    out = torch.full_like(q, float("nan"))
+    mask = mask0.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        att.step(q, k, v, out, mask, -3.0, 1)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        mask.copy_(mask0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ro) and torch.equal(mask, rm), f"replay {rep}"
+        _run(att, q, k, v, mask0, -2.0, 0)        # eager work between replays
+        torch.cuda.synchronize()
