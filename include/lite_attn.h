@@ -34,7 +34,9 @@
  *   results, no queue) when all 64 queues of the device are taken, for the per-thread
  *   default stream, and when the stream belongs to a device other than the current one.
  *   A stream must not be destroyed while its steps are still running (its handle value
- *   could then be reused by a new stream while the queue is in use).
+ *   could then be reused by a new stream while the queue is in use). A step captured into a
+ *   graph keeps the queue of the stream it was captured on: replay it so that it does not
+ *   overlap steps launched on that stream.
  */
 #ifndef LITE_ATTN_H
 #define LITE_ATTN_H
