@@ -7,22 +7,25 @@
 // maximum is flagged, and the flag persists across denoising steps) and "Architecture
 // Overview" (bitmask, skip logic inside the FlashAttention softmax pipeline).
 //
-// Work decomposition. One workgroup owns one query tile (b, h, i) and is the only reader and
-// writer of that tile's mask row, so no global atomics are needed. Each 64-lane wave owns 32
-// query rows. Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-// the accumulator then holds one query per lane (lane % 32) and 16 keys per register group,
-// so the row maximum and row sum of the online softmax are in-lane reductions plus a single
-// swap between the two half-waves (v_permlane32_swap). The PV product is likewise computed
+// Work decomposition. A workgroup owns one query tile (b, h, i) at a time and is the only reader
+// and writer of that tile's mask row, so the mask needs no atomics. The grid is persistent:
+// workgroups take tiles from a queue, one atomic add per tile. Each 64-lane wave owns 32 query
+// rows. Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: the
+// accumulator then holds one query per lane (lane % 32) and 16 keys per register group, so the
+// row maximum and row sum of the online softmax are in-lane reductions plus a single swap
+// between the two half-waves (v_permlane32_swap). The PV product is likewise computed
 // transposed, O^T += V^T P^T, which takes P straight from the score registers (converted to
-// bf16) as the B operand; V is stored transposed in LDS so that the A operand is one 16-byte
-// LDS read per lane. The key order inside a 16-key MFMA step is permuted identically on both
-// operands, which leaves the contraction unchanged.
+// bf16) as the B operand; V stays row-major in LDS and the A operand is read with
+// ds_read_b64_tr_b16, which transposes as it reads. The key order
+// inside a 16-key MFMA step is permuted identically on both operands, which leaves the
+// contraction unchanged.
 //
 // The QK-Skip vote needs nothing beyond the online softmax: the tile's row maximum mt is
 // already computed for the rescale, and the running maximum m is the softmax state. A wave
-// votes "keep" when any of its valid rows has (mt - m) * scale >= log_eps (or NaN); the votes
-// of the workgroup's waves are OR-ed into an LDS bitset, and the tile is flagged at the end
-// when no wave voted keep.
+// votes "keep" when any of its valid rows has (mt - m) * scale >= log_eps (or NaN). Each wave
+// collects its votes as scalar bits by position in the visiting list; after the tile loop the
+// workgroup ORs them, and a visited tile is flagged when no wave voted keep. (With in-step skip
+// the votes go to an LDS bitset at once, since later tiles of the same step read them.)
 //
 // Skipped tiles cost nothing: the mask row is turned into a compact visiting list in LDS
 // before any K/V load, and the K/V pipeline only ever fetches listed tiles.
