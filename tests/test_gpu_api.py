@@ -213,3 +213,24 @@ def test_largest_supported_length():
         c.add_out(got[0, 0, r0:r1], ref.out[0, 0, r0:r1])
         c.add_mask(gbits[0, 0, i], rbits[0, 0, i], ref.margins[0, 0, i], bits[0, 0, i])
     c.check("N=131072")
+
+
+@pytest.mark.parametrize("tile_q,D,P", [(64, 64, 200), (64, 128, 64), (128, 64, 1100), (128, 128, 2000)])
+def test_dense_prefix_order_shapes(tile_q, D, P):
+    """The persistent launch hands out the dense-prefix query tiles first (ceil(P / tile_q) per
+    head, over all batches and heads), then the rest in traversal direction. Every tile must
+    still be computed exactly once: a random prior mask, both traversal directions, B = 2,
+    H = 3, and prefixes of under one tile, exactly one tile, several tiles and the whole
+    sequence (P = N)."""
+    n = 2000 if P <= 2000 else P
+    B, H = 2, 3
+    tq, tk, w = mask_geometry(n, tile_q, 64)
+    rng = np.random.default_rng(tile_q * 1000 + D + P)
+    bits = rng.random((B, H, tq, tk)) < 0.4
+    for step in (0, 1):
+        out, m, ref = _step_both(B, H, n, D, torch.bfloat16, bits_to_mask(bits), -2.0, step,
+                                 tile_q=tile_q, prefix=P, seed=31 + step, spread=2.0)
+        c = Comparison()
+        c.add_out(out, ref.out)
+        c.add_mask(mask_to_bits(m, tk), mask_to_bits(ref.mask_next, tk), ref.margins, bits)
+        c.check(f"prefix order tq={tile_q} D={D} P={P} step {step}")
