@@ -87,3 +87,23 @@ def test_scheduled_full_size_order_and_result():
     assert set(prefix_tiles) <= set(perm[:n_heavy].tolist())
     wl.drop_cache()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("label,cid,kw,steps", CASES[:2], ids=[c[0] + "_in_step" for c in CASES[:2]])
+def test_scheduled_in_step_matches_plain_in_step(label, cid, kw, steps):
+    """The schedule composes with in-step skip: with the option on, the scheduled step equals the
+    plain step bit for bit."""
+    dev = device()
+    cfg = derive(get_config(cid), name=label + "_ins", steps=steps, **kw)
+    wl = Workload(cfg, dev)
+    att = make_attention(cfg, in_step_skip=True)
+    ws = att.new_workspace(dev)
+    m_plain, m_sched = att.new_mask(dev), att.new_mask(dev)
+    for t in range(steps):
+        q, k, v = wl.inputs(t)
+        o_plain, o_sched = torch.empty_like(q), torch.empty_like(q)
+        att.step(q, k, v, o_plain, m_plain, cfg.log_eps[t], t)
+        att.step(q, k, v, o_sched, m_sched, cfg.log_eps[t], t, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o_plain, o_sched), f"{label} step {t}: outputs differ"
+        assert torch.equal(m_plain, m_sched), f"{label} step {t}: masks differ"
