@@ -72,6 +72,10 @@ def parse_args():
     ap.add_argument("--in-step-skip", action="store_true",
                     help="enable the in-step-skip option (tiles flagged in a step also leave that "
                          "step's output; their exponentials and PV are not computed)")
+    ap.add_argument("--repeats", type=int, default=0, metavar="R",
+                    help="also time every step of one generation R times, restoring the mask "
+                         "(and tile statistics) from a saved copy before each repeat, outside the "
+                         "timed events; reports the per-step medians and a fit over them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -131,6 +135,57 @@ def linear_fit(xs, ys):
     ss_tot = sum((y - my) ** 2 for y in ys)
     ss_res = sum((y - (a * x + b)) ** 2 for x, y in zip(xs, ys))
     return a, b, (1.0 - ss_res / ss_tot) if ss_tot > 0 else None
+
+
+def per_step_medians(att, cfg, qs, ks, v, out, log_eps, stream, dev, args, workspace, tiles_q,
+                     tiles_k):
+    """Per-step timing protocol: along one generation from an empty mask, step t is launched R
+    times, each time from the mask (and tile statistics) saved before its first launch; the
+    restore is a device copy outside the timed events. Returns the median and spread of each
+    step's launch time, the rates at the median, and the fit t = t_dense (1 - s) + t0 over the
+    medians."""
+    import statistics
+    import torch
+    R = args.repeats
+    refresh = args.refresh_delta is not None
+    mask = att.new_mask(dev)
+    att.reset_mask(mask)
+    stats = att.new_tile_stats(dev) if refresh else None
+    if refresh:
+        stats.fill_(float("nan"))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = []
+    for t in range(cfg.steps):
+        saved = mask.clone()
+        saved_stats = stats.clone() if refresh else None
+        f, kvb, sfrac = computed_work(mask, cfg, tiles_q, tiles_k)
+        times = []
+        for _ in range(R):
+            mask.copy_(saved)
+            if refresh:
+                stats.copy_(saved_stats)
+            e0.record(stream)
+            if refresh:
+                att.step(qs[t], ks[t], v, out, mask, log_eps[t], t, tile_stats=stats,
+                         refresh_delta=args.refresh_delta)
+            else:
+                att.step(qs[t], ks[t], v, out, mask, log_eps[t], t, workspace=workspace)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        if args.in_step_skip:
+            # tiles flagged during the step were scored but got no PV product
+            f_after, _, _ = computed_work(mask, cfg, tiles_q, tiles_k)
+            f = f_after + 0.5 * (f - f_after)
+        med = statistics.median(times)
+        rows.append({"t": t, "skipped": round(sfrac, 4), "kernel_ms_median": round(med, 4),
+                     "kernel_ms_min": round(min(times), 4), "kernel_ms_max": round(max(times), 4),
+                     "computed_tflops": round(f / (med * 1e-3) / 1e12, 2),
+                     "kv_gbs_requested": round(kvb / (med * 1e-3) / 1e9, 1)})
+    a, b0, r2 = linear_fit([1.0 - r["skipped"] for r in rows], [r["kernel_ms_median"] for r in rows])
+    return {"repeats": R, "steps": rows,
+            "time_fit": None if a is None else {"t_dense_ms": round(a, 3), "t0_ms": round(b0, 3),
+                                                "r2": None if r2 is None else round(r2, 4)}}
 
 
 def cpu_baseline(cfg, qs, ks, v, budget_s: float):
@@ -347,6 +402,9 @@ def main():
         "flops_per_launch_mean": sum(flops) / len(flops),
         "kernel_source_hash": khash,
     }
+    if args.repeats > 0:
+        result_repeats = per_step_medians(att, cfg, qs, ks, v, out, log_eps, stream, dev, args,
+                                          workspace, tiles_q, tiles_k)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")
@@ -394,6 +452,8 @@ def main():
                               "r2": None if r2 is None else round(r2, 4)}
     if calibration is not None:
         result["calibration"] = calibration
+    if args.repeats > 0:
+        result["per_step_repeats"] = result_repeats
     if args.per_step:
         result["per_step"] = [
             {"t": (warmup + s) % cfg.steps, "kernel_ms": round(kernel_ms[s], 4),
