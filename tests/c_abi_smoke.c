@@ -5,7 +5,10 @@
  *   - every output element is finite, and every output row is a convex combination of V rows,
  *     so it lies inside the per-column range of V;
  *   - the skipped-tile count never decreases along the chain (flags persist);
- *   - running the same chain twice gives bit-identical outputs and masks.
+ *   - running the same chain twice gives bit-identical outputs and masks;
+ *   - the same chain through lite_attn_step_scheduled (heaviest-first order, caller workspace)
+ *     and through lite_attn_step_refresh with refresh_delta = +inf (references start as NaN)
+ *     gives the plain chain's outputs and masks bit for bit.
  * Exit status 0 means every check passed; the last line printed says "c abi smoke ok".
  * Built by tests/test_c_abi.py with hipcc (host code only) and linked against the library.
  */
@@ -71,14 +74,29 @@ static void fill(uint16_t* x, size_t n, uint64_t seed, float a) {
   }
 }
 
-static int run_chain(lite_attn_t h, const void* dq, const void* dk, const void* dv, void* dout,
-                     uint32_t* dmask, uint32_t* dcounts, uint16_t* out_host, uint32_t* mask_host,
-                     size_t mask_bytes, uint64_t* skipped) {
+enum { PLAIN = 0, SCHEDULED = 1, REFRESH = 2 };
+
+static int run_chain(lite_attn_t h, int mode, const void* dq, const void* dk, const void* dv,
+                     void* dout, uint32_t* dmask, uint32_t* dcounts, void* dws, float* dstats,
+                     uint16_t* out_host, uint32_t* mask_host, size_t mask_bytes,
+                     uint64_t* skipped) {
   static const float eps[STEPS] = {-INFINITY, -3.0f, -2.5f, -2.0f};
   CHECK_LA(lite_attn_reset_mask(h, dmask, NULL));
+  if (mode == REFRESH) {
+    float nan_stats[B * H * 32];   /* Tq = ceil(N / 128) = 24 query tiles per head */
+    for (int i = 0; i < B * H * 32; ++i) nan_stats[i] = NAN;
+    CHECK_HIP(hipMemcpy(dstats, nan_stats, sizeof(float) * B * H * ((N + 127) / 128),
+                        hipMemcpyHostToDevice));
+  }
   uint64_t prev = 0;
   for (int t = 0; t < STEPS; ++t) {
-    CHECK_LA(lite_attn_step(h, dq, dk, dv, dout, dmask, eps[t], t, NULL));
+    if (mode == SCHEDULED)
+      CHECK_LA(lite_attn_step_scheduled(h, dq, dk, dv, dout, dmask, eps[t], t, dws, NULL));
+    else if (mode == REFRESH)
+      CHECK_LA(lite_attn_step_refresh(h, dq, dk, dv, dout, dmask, dstats, INFINITY, eps[t], t,
+                                      NULL));
+    else
+      CHECK_LA(lite_attn_step(h, dq, dk, dv, dout, dmask, eps[t], t, NULL));
     CHECK_LA(lite_attn_mask_popcount(h, dmask, dcounts, NULL));
     uint32_t counts[B * H];
     CHECK_HIP(hipMemcpy(counts, dcounts, sizeof counts, hipMemcpyDeviceToHost));
@@ -90,7 +108,7 @@ static int run_chain(lite_attn_t h, const void* dq, const void* dk, const void* 
       return 4;
     }
     prev = total;
-    printf("step %d: skipped tiles %llu\n", t, (unsigned long long)total);
+    printf("chain %d step %d: skipped tiles %llu\n", mode, t, (unsigned long long)total);
   }
   *skipped = prev;
   CHECK_HIP(hipMemcpy(out_host, dout, sizeof(uint16_t) * (size_t)B * H * N * D,
@@ -140,18 +158,30 @@ int main(void) {
   uint32_t* m1 = (uint32_t*)malloc(mask_bytes);
   uint32_t* m2 = (uint32_t*)malloc(mask_bytes);
   if (!q || !k || !v || !out1 || !out2 || !m1 || !m2) return 7;
+  if (tq > 32) {
+    fprintf(stderr, "more query tiles per head than the statistics buffer holds\n");
+    return 7;
+  }
   fill(q, elems, 1, 2.0f);
   fill(k, elems, 2, 2.0f);
   fill(v, elems, 3, 1.0f);
 
-  void *dq, *dk, *dv, *dout;
+  void *dq, *dk, *dv, *dout, *dws;
   uint32_t *dmask, *dcounts;
+  float* dstats;
+  const size_t ws_bytes = lite_attn_workspace_bytes(h);
+  if (ws_bytes == 0) {
+    fprintf(stderr, "lite_attn_workspace_bytes returned 0\n");
+    return 6;
+  }
   CHECK_HIP(hipMalloc(&dq, elems * 2));
   CHECK_HIP(hipMalloc(&dk, elems * 2));
   CHECK_HIP(hipMalloc(&dv, elems * 2));
   CHECK_HIP(hipMalloc(&dout, elems * 2));
   CHECK_HIP(hipMalloc((void**)&dmask, mask_bytes));
   CHECK_HIP(hipMalloc((void**)&dcounts, sizeof(uint32_t) * B * H));
+  CHECK_HIP(hipMalloc(&dws, ws_bytes));
+  CHECK_HIP(hipMalloc((void**)&dstats, sizeof(float) * B * H * tq));
   CHECK_HIP(hipMemcpy(dq, q, elems * 2, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dk, k, elems * 2, hipMemcpyHostToDevice));
   CHECK_HIP(hipMemcpy(dv, v, elems * 2, hipMemcpyHostToDevice));
@@ -167,13 +197,17 @@ int main(void) {
   }
 
   uint64_t s1 = 0, s2 = 0;
-  int rc = run_chain(h, dq, dk, dv, dout, dmask, dcounts, out1, m1, mask_bytes, &s1);
+  int rc = run_chain(h, PLAIN, dq, dk, dv, dout, dmask, dcounts, dws, dstats, out1, m1,
+                     mask_bytes, &s1);
   if (rc) return rc;
-  rc = run_chain(h, dq, dk, dv, dout, dmask, dcounts, out2, m2, mask_bytes, &s2);
-  if (rc) return rc;
-  if (memcmp(out1, out2, elems * 2) != 0 || memcmp(m1, m2, mask_bytes) != 0 || s1 != s2) {
-    fprintf(stderr, "two runs of the same chain differ\n");
-    return 9;
+  for (int mode = PLAIN; mode <= REFRESH; ++mode) {
+    rc = run_chain(h, mode, dq, dk, dv, dout, dmask, dcounts, dws, dstats, out2, m2, mask_bytes,
+                   &s2);
+    if (rc) return rc;
+    if (memcmp(out1, out2, elems * 2) != 0 || memcmp(m1, m2, mask_bytes) != 0 || s1 != s2) {
+      fprintf(stderr, "chain %d differs from the plain chain\n", mode);
+      return 9;
+    }
   }
   if (s1 == 0) {
     fprintf(stderr, "no tile was skipped: the chain did not exercise skipping\n");
@@ -208,6 +242,8 @@ int main(void) {
   CHECK_HIP(hipFree(dout));
   CHECK_HIP(hipFree(dmask));
   CHECK_HIP(hipFree(dcounts));
+  CHECK_HIP(hipFree(dws));
+  CHECK_HIP(hipFree(dstats));
   CHECK_LA(lite_attn_destroy(h));
   free(q); free(k); free(v); free(out1); free(out2); free(m1); free(m2);
   printf("c abi smoke ok: %llu of %lld tiles skipped after %d steps\n", (unsigned long long)s1,

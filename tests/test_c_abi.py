@@ -2,7 +2,8 @@
 include/lite_attn.h and linked against liblite_attn.so (no Python, torch or HIP compiler in
 between). On the CPU it must compile and link; on the GPU it must run a short chain and pass its
 own checks (finite outputs inside the range of V, a non-decreasing skip count, bit-identical
-reruns, argument errors reported)."""
+reruns, argument errors reported, and the scheduled and refresh entry points reproducing the
+plain chain bit for bit)."""
 import os
 import shutil
 import subprocess
