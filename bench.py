@@ -188,6 +188,20 @@ def per_step_medians(att, cfg, qs, ks, v, out, log_eps, stream, dev, args, works
                                                 "r2": None if r2 is None else round(r2, 4)}}
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: logical CPUs and the processor model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "model": model}
+
+
 def cpu_baseline(cfg, qs, ks, v, budget_s: float):
     """Time the CPU oracle on whole query tiles of step 0 until `budget_s` is spent."""
     import numpy as np
@@ -226,6 +240,7 @@ def cpu_baseline(cfg, qs, ks, v, budget_s: float):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": host_cpu(),
         "sample": f"{done} query tiles of step 0 of {cfg.name} (batch {b}, head {h}), float64 "
                   f"numpy oracle, {dt:.1f} s; dense-equivalent flops of those tiles / time",
     }

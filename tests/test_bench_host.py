@@ -75,3 +75,9 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_host_cpu_names_the_processor():
+    h = bench.host_cpu()
+    assert h["nproc"] == os.cpu_count()
+    assert h["model"] is None or isinstance(h["model"], str)
