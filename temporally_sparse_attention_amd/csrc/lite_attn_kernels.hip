@@ -794,7 +794,10 @@ __device__ __attribute__((noinline)) void bf16_tiles(uint64_t args) {
         pos = (r / (Tq - P)) * Tq + P + r % (Tq - P);
       }
     }
-    bf16_tile_body<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos);
+    // At D = 128 and tile_q 64 the tile runs one wave per SIMD at 256 VGPRs; inlined into this
+    // loop it lost its pinned MFMA/VALU interleave, so there it is called once per tile.
+    if constexpr (D == 128 && NW == 2) bf16_tile<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos);
+    else bf16_tile_body<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos);
     __syncthreads();           // LDS and s_next are reused by the next tile
   }
 #endif  // __HIP_DEVICE_COMPILE__
