@@ -82,7 +82,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
-            "(python -m temporally_sparse_attention_amd.build or __graft_entry__.build())")
+            "(python -m temporally_sparse_attention_amd.build)")
     # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) but loads it by
     # another file name. Loading torch first makes this library bind to that runtime instead of
     # bringing a second HIP/HSA runtime into the process (a second runtime sees no device).

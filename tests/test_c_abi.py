@@ -21,7 +21,7 @@ def _build(tmp_path):
     if gcc is None:
         pytest.skip("gcc not available")
     if not os.path.exists(os.path.join(LIBDIR, "liblite_attn.so")):
-        pytest.fail("liblite_attn.so is not built (run __graft_entry__.build())")
+        pytest.fail("liblite_attn.so is not built (run python -m temporally_sparse_attention_amd.build)")
     exe = str(tmp_path / "c_abi_smoke")
     cmd = [gcc, "-O2", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
            f"-I{ROCM}/include", f"-I{os.path.join(ROOT, 'include')}", SRC, "-o", exe,
