@@ -28,15 +28,19 @@
  *   differ.
  * - bf16 steps run as persistent launches: a grid of as many workgroups as the device holds
  *   at once takes query tiles from a tile queue, a pair of uint32 in the library's static
- *   device memory. Each (device, stream) pair is given one of 64 queues per device on first
- *   use and keeps it; launches on one stream run one after another, and each launch leaves
- *   its queue at zero when it ends. A step falls back to one workgroup per query tile (same
- *   results, no queue) when all 64 queues of the device are taken, for the per-thread
- *   default stream, and when the stream belongs to a device other than the current one.
- *   A stream must not be destroyed while its steps are still running (its handle value
- *   could then be reused by a new stream while the queue is in use). A step captured into a
- *   graph keeps the queue of the stream it was captured on: replay it so that it does not
- *   overlap steps launched on that stream.
+ *   device memory. Launches that share a queue must not overlap, so queues are handed out
+ *   this way:
+ *   - an eager step uses the queue of its (device, stream) pair: each of up to 64 streams per
+ *     device is given one on first use and keeps it (steps on one stream run in order);
+ *   - a step captured into a HIP graph is given a queue of its own (up to 4032 captured steps
+ *     per device over the life of the process), so a graph may be replayed on any stream,
+ *     concurrently with other steps that use other masks;
+ *   - without a queue (more than 64 streams, more captured steps than queues, the per-thread
+ *     default stream, or a stream of a device other than the current one) a step launches
+ *     one workgroup per query tile instead, with the same results.
+ *   Each launch leaves its queue at zero when it ends. A stream must not be destroyed while
+ *   its steps are still running (its handle value could then be reused by a new stream while
+ *   the queue is in use). lite_attn_last_launch() reports how the last step was launched.
  */
 #ifndef LITE_ATTN_H
 #define LITE_ATTN_H
@@ -109,8 +113,9 @@ typedef struct lite_attn_s* lite_attn_t;
 /* Validate `cfg` and create a handle (host memory only; no device call).
  * LiteAttention, page 1 "Architecture Overview": the Skip-Mask bitmask and QK-Skip.
  * Returns INVALID_ARG for NULL arguments, a wrong abi_version, negative sizes, strides that
- * are not multiples of 8 elements, dense_prefix outside [0, seq_len], unknown option bits or
- * a nonzero reserved field; UNSUPPORTED for a
+ * are not multiples of 8 elements, strides under which two (b, h, n) rows of out would overlap
+ * (out is written through the shared strides), dense_prefix outside [0, seq_len], unknown
+ * option bits or a nonzero reserved field; UNSUPPORTED for a
  * head_dim / tile / dtype combination without a kernel or for Tk > 2048 (N > 131072 with
  * 64-key tiles). On failure *out is set to NULL. */
 int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out);
@@ -215,6 +220,12 @@ const char* lite_attn_status_string(int status);
 
 /* Message describing the most recent failure on the calling thread ("" if none). */
 const char* lite_attn_last_error(void);
+
+/* How the calling thread's most recent step call launched its attention kernel (diagnostics):
+ * *workgroups receives the grid size and *queue the tile queue it used, -1 when it took one
+ * workgroup per query tile without a queue (see the conventions above). Before any launch on
+ * the thread: 0 and -1. Either pointer may be NULL. Always returns OK. */
+int lite_attn_last_launch(int32_t* workgroups, int32_t* queue);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     lite_attn_create,
     lite_attn_destroy,
     lite_attn_last_error,
+    lite_attn_last_launch,
     lite_attn_mask_bytes,
     lite_attn_mask_geometry,
     lite_attn_mask_popcount,

@@ -34,6 +34,7 @@ EXPORTS = (
     "lite_attn_mask_popcount",
     "lite_attn_status_string",
     "lite_attn_last_error",
+    "lite_attn_last_launch",
 )
 
 
@@ -120,6 +121,8 @@ def _load() -> ctypes.CDLL:
     lib.lite_attn_status_string.restype = ctypes.c_char_p
     lib.lite_attn_last_error.argtypes = []
     lib.lite_attn_last_error.restype = ctypes.c_char_p
+    lib.lite_attn_last_launch.argtypes = [i32p, i32p]
+    lib.lite_attn_last_launch.restype = ctypes.c_int
     del u32p
     return lib
 
@@ -137,6 +140,14 @@ def lite_attn_status_string(status: int) -> str:
 
 def lite_attn_last_error() -> str:
     return _lib.lite_attn_last_error().decode()
+
+
+def lite_attn_last_launch() -> Tuple[int, int]:
+    """(workgroups, queue) of the calling thread's most recent step launch; queue -1: one
+    workgroup per query tile, no tile queue."""
+    wg, qu = ctypes.c_int32(), ctypes.c_int32()
+    _lib.lite_attn_last_launch(ctypes.byref(wg), ctypes.byref(qu))
+    return wg.value, qu.value
 
 
 def _check(status: int, what: str):

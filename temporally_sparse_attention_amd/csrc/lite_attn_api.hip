@@ -43,18 +43,24 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile queue of a stream for persistent launches. Each (device, stream) pair gets one of the
-// device's kQueueSlots queues for the life of the process; launches on one stream run one after
-// another, so a queue is never used by two launches at once. Returns nullptr (the launch then
-// takes one workgroup per tile) when the stream belongs to another device than the current
-// one, for the per-thread default stream (one handle value, many streams), or when every queue
-// of the device is taken.
+// Tile queue of a persistent launch. Two launches that share a queue must not overlap: each
+// takes tile positions from it, and the last workgroup of each puts it back to zero.
+// - An eager launch uses the queue of its (device, stream) pair, one of the device's first
+//   kEagerQueueSlots queues, assigned on first use and kept for the life of the process.
+//   Launches on one stream run one after another.
+// - A launch captured into a graph gets a queue of its own, never given to anything else: a
+//   graph may be replayed on any stream, concurrently with other work (two guidance branches
+//   captured on one capture stream and replayed on two streams, say).
+// Returns nullptr (the launch then takes one workgroup per query tile) when the stream belongs
+// to another device than the current one, for the per-thread default stream (one handle value,
+// many streams), or when the pool the launch draws from is used up.
 struct QueueTable {
   std::mutex mu;
   std::map<std::pair<int, uintptr_t>, int> slot;
-  std::map<int, int> used;
+  std::map<int, int> used;        // eager queues handed out, per device
+  std::map<int, int> captured;    // captured-launch queues handed out, per device
   std::map<int, int> cus;
-  std::map<int, uint32_t*> base;   // queue 0 of each device
+  std::map<int, uint32_t*> base;  // queue 0 of each device
 };
 
 QueueTable& queue_table() {
@@ -62,14 +68,17 @@ QueueTable& queue_table() {
   return *t;
 }
 
-uint32_t* stream_queue(hipStream_t st, int* n_cu) {
+uint32_t* launch_queue(hipStream_t st, int* n_cu, int* slot_out) {
   *n_cu = 0;
+  *slot_out = -1;
   if (st == hipStreamPerThread) return nullptr;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
   if (st != nullptr) {
     int dev = -1;
     if (hipStreamGetDevice(st, &dev) != hipSuccess || dev != cur) return nullptr;
+    if (hipStreamIsCapturing(st, &capture) != hipSuccess) return nullptr;
   }
   QueueTable& t = queue_table();
   std::lock_guard<std::mutex> lock(t.mu);
@@ -80,21 +89,59 @@ uint32_t* stream_queue(hipStream_t st, int* n_cu) {
       return nullptr;
     c = t.cus.emplace(cur, n).first;
   }
-  const auto key = std::make_pair(cur, reinterpret_cast<uintptr_t>(st));
-  auto it = t.slot.find(key);
-  if (it == t.slot.end()) {
-    int& used = t.used[cur];
-    if (used >= lite_attn::kQueueSlots) return nullptr;
-    it = t.slot.emplace(key, used++).first;
-  }
   auto b = t.base.find(cur);
   if (b == t.base.end()) {
     uint32_t* q0 = nullptr;
     if (lite_attn::tile_queue_address(0, &q0) != hipSuccess) return nullptr;
     b = t.base.emplace(cur, q0).first;
   }
+  int slot;
+  if (capture == hipStreamCaptureStatusActive) {
+    int& n = t.captured[cur];
+    if (n >= lite_attn::kQueueSlots - lite_attn::kEagerQueueSlots) return nullptr;
+    slot = lite_attn::kEagerQueueSlots + n++;
+  } else {
+    const auto key = std::make_pair(cur, reinterpret_cast<uintptr_t>(st));
+    auto it = t.slot.find(key);
+    if (it == t.slot.end()) {
+      int& used = t.used[cur];
+      if (used >= lite_attn::kEagerQueueSlots) return nullptr;
+      it = t.slot.emplace(key, used++).first;
+    }
+    slot = it->second;
+  }
   *n_cu = c->second;
-  return b->second + 2 * it->second;
+  *slot_out = slot;
+  return b->second + 2 * slot;
+}
+
+// The most recent attention launch of the calling thread (lite_attn_last_launch).
+thread_local int32_t g_last_grid = 0;
+thread_local int32_t g_last_queue = -1;
+
+// out is written through the strides it shares with q, k and v, so the map from (b, h, n, d)
+// to an element offset must be one to one: every dimension with more than one index needs a
+// nonzero stride, and, taken in increasing stride order, each stride must reach past the span
+// of the dimension before it (the head dimension is the innermost, stride 1).
+bool strides_one_to_one(int64_t B, int64_t H, int64_t N, int64_t D, int64_t sb, int64_t sh,
+                        int64_t sn) {
+  struct Dim {
+    int64_t extent, stride;
+  } dims[4] = {{D, 1}, {N, sn}, {H, sh}, {B, sb}};
+  Dim live[4];
+  int n = 0;
+  for (const Dim& d : dims) {
+    if (d.extent <= 1) continue;
+    if (d.stride <= 0) return false;
+    live[n++] = d;
+  }
+  for (int i = 1; i < n; ++i)   // insertion sort by stride
+    for (int j = i; j > 0 && live[j].stride < live[j - 1].stride; --j) std::swap(live[j], live[j - 1]);
+  for (int i = 1; i < n; ++i) {
+    const __int128 span = (__int128)live[i - 1].stride * live[i - 1].extent;
+    if ((__int128)live[i].stride < span) return false;
+  }
+  return true;
 }
 
 }  // namespace
@@ -113,6 +160,12 @@ const char* lite_attn_status_string(int status) {
 }
 
 const char* lite_attn_last_error(void) { return g_last_error.c_str(); }
+
+int lite_attn_last_launch(int32_t* workgroups, int32_t* queue) {
+  if (workgroups) *workgroups = g_last_grid;
+  if (queue) *queue = g_last_queue;
+  return LITE_ATTN_OK;
+}
 
 int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
   try {
@@ -150,6 +203,11 @@ int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
       return fail(LITE_ATTN_ERR_INVALID_ARG,
                   "create: strides (%lld, %lld, %lld) must be non-negative multiples of 8 "
                   "elements with head_dim <= stride_n < 2^24",
+                  (long long)sb, (long long)sh, (long long)sn);
+    if (!strides_one_to_one(c.batch, c.heads, c.seq_len, c.head_dim, sb, sh, sn))
+      return fail(LITE_ATTN_ERR_INVALID_ARG,
+                  "create: strides (%lld, %lld, %lld) map two (b, h, n) rows of out to "
+                  "overlapping memory",
                   (long long)sb, (long long)sh, (long long)sn);
 
     if (c.tile_k != lite_attn::kTileK)
@@ -263,7 +321,8 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     p.perm = nullptr;
     p.stats = refresh ? tile_stats : nullptr;
     p.refresh_delta = refresh_delta;
-    p.queue = c.dtype == LITE_ATTN_BF16 ? stream_queue(st, &p.n_cu) : nullptr;   // persistent
+    int slot = -1;
+    p.queue = c.dtype == LITE_ATTN_BF16 ? launch_queue(st, &p.n_cu, &slot) : nullptr;
     if (!p.queue) p.n_cu = 0;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;
@@ -273,9 +332,12 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
                     hipGetErrorString(e));
       p.perm = static_cast<const uint32_t*>(workspace);
     }
-    const hipError_t e = h->fwd(p, st);
+    unsigned grid = 0;
+    const hipError_t e = h->fwd(p, st, &grid);
     if (e != hipSuccess)
       return fail(LITE_ATTN_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+    g_last_grid = (int32_t)grid;
+    g_last_queue = p.queue ? slot : -1;
     return LITE_ATTN_OK;
   } catch (...) {
     return fail(LITE_ATTN_ERR_HIP, "%s: unexpected exception", who);

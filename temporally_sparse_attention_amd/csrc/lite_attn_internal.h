@@ -9,7 +9,10 @@ namespace lite_attn {
 constexpr int kTileK = 64;          // keys per tile (two 32-key MFMA blocks)
 constexpr int kMaxTilesK = 2048;    // visiting list capacity per query tile (LDS)
 constexpr int kMaxWords = kMaxTilesK / 32;
-constexpr int kQueueSlots = 64;     // tile queues per device for persistent launches
+// Tile queues per device for persistent launches: the first kEagerQueueSlots go to streams
+// (one per stream), the rest to launches captured into graphs (one per captured launch).
+constexpr int kQueueSlots = 4096;
+constexpr int kEagerQueueSlots = 64;
 
 // Everything one forward launch needs. Strides are in elements.
 struct FwdParams {
@@ -36,7 +39,8 @@ struct FwdParams {
   int n_cu;
 };
 
-using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t);
+// Launches the attention kernel; *grid receives the number of workgroups launched.
+using FwdLauncher = hipError_t (*)(const FwdParams&, hipStream_t, unsigned* grid);
 
 // Launcher for (dtype, head_dim, tile_q, in-step skip) or nullptr when no kernel is built for
 // it. dtype: 0 = bf16, 1 = fp32.

@@ -1099,7 +1099,7 @@ __global__ void __launch_bounds__(256) mask_popcount(const uint32_t* mask, uint3
 // hipLaunchKernel reports the status of this launch only (hipGetLastError would also return
 // errors left behind by other HIP users in the process).
 template <int D, int NW, bool INSTEP>
-hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_bf16(const FwdParams& p, hipStream_t stream, unsigned* grid_out) {
   const unsigned tiles = (unsigned)((int64_t)p.B * p.H * p.Tq);
   unsigned grid = tiles;
   if (p.queue != nullptr) {
@@ -1115,6 +1115,7 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
     const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * (p.n_cu > 0 ? p.n_cu : 1);
     if (resident < (int64_t)grid) grid = (unsigned)resident;
   }
+  *grid_out = grid;
   FwdParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_bf16<D, NW, INSTEP>),
@@ -1122,8 +1123,9 @@ hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
 }
 
 template <int D, int NW, bool INSTEP>
-hipError_t launch_f32(const FwdParams& p, hipStream_t stream) {
+hipError_t launch_f32(const FwdParams& p, hipStream_t stream, unsigned* grid_out) {
   const unsigned grid = (unsigned)((int64_t)p.B * p.H * p.Tq);
+  *grid_out = grid;
   FwdParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(reinterpret_cast<const void*>(&lite_attn_fwd_f32<D, NW, INSTEP>),

@@ -52,12 +52,16 @@ class Comparison:
 
     def add_mask(self, gpu_bits: np.ndarray, ref_bits: np.ndarray, margins: np.ndarray,
                  start_bits: np.ndarray):
+        """Adds one step's mask comparison; returns that step's (mismatches beyond the margin
+        band, near-threshold tiles, near-threshold tiles that differ)."""
         near = np.abs(np.nan_to_num(margins, nan=np.inf)) <= MARGIN_BAND
         diff = gpu_bits != ref_bits
-        self.near += int(near.sum())
-        self.mismatch += int((diff & ~near).sum())
+        step = (int((diff & ~near).sum()), int(near.sum()), int((diff & near).sum()))
+        self.near += step[1]
+        self.mismatch += step[0]
         self.tiles += gpu_bits.size
         self.flags += int((ref_bits & ~start_bits).sum())
+        return step
 
     @property
     def mean_abs(self):
@@ -81,9 +85,10 @@ def make_attention(cfg, **over):
 
 
 def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=None,
-                         scale=None, label="", log_eps=None, in_step_skip=False):
+                         scale=None, label="", log_eps=None, in_step_skip=False, workspace=None):
     """Run `steps` steps. Before each step the GPU mask rows under test are overwritten with
-    the oracle's mask; outputs and new mask rows are compared on `rows` (default: all)."""
+    the oracle's mask; outputs and new mask rows are compared on `rows` (default: all). With a
+    workspace the GPU runs the scheduled step (lite_attn_step_scheduled)."""
     dev = workload.device
     order = order or cfg.order
     scale = cfg.softmax_scale if scale is None else scale
@@ -108,7 +113,7 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
             cur = from_mask_tensor(gpu_mask)
             cur[sel] = ref_mask[sel]
             gpu_mask.copy_(to_mask_tensor(cur, dev))
-        att.step(q, k, v, out, gpu_mask, le, t)
+        att.step(q, k, v, out, gpu_mask, le, t, workspace=workspace)
         torch.cuda.synchronize()
         qc, kc, vc = (q.cpu(), k.cpu(), v.cpu()) if sel is None else (q, k, v)
         if sel is not None:
@@ -137,8 +142,8 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
                 r0, r1 = i * att.handle.cfg.tile_q, min(cfg.seq_len, (i + 1) * att.handle.cfg.tile_q)
                 cmp.add_out(gout[b, h, r0:r1], ref_out[b, h, r0:r1])
             gbits = mask_to_bits(from_mask_tensor(gpu_mask), tk)[sel]
-            cmp.add_mask(gbits, mask_to_bits(new_mask, tk)[sel], margins[sel],
-                         mask_to_bits(ref_mask, tk)[sel])
+            per_step = cmp.add_mask(gbits, mask_to_bits(new_mask, tk)[sel], margins[sel],
+                                    mask_to_bits(ref_mask, tk)[sel])
             ref_mask = new_mask
         else:
             ref = lite_attn_step_ref(qc, kc, vc, ref_mask, tile_q=att.handle.cfg.tile_q,
@@ -146,10 +151,14 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
                                      order=order, dense_prefix=cfg.dense_prefix,
                                      in_step_skip=in_step_skip)
             cmp.add_out(out.double().cpu().numpy(), ref.out)
-            cmp.add_mask(mask_to_bits(from_mask_tensor(gpu_mask), tk),
-                         mask_to_bits(ref.mask_next, tk), ref.margins,
-                         mask_to_bits(ref_mask, tk))
+            per_step = cmp.add_mask(mask_to_bits(from_mask_tensor(gpu_mask), tk),
+                                    mask_to_bits(ref.mask_next, tk), ref.margins,
+                                    mask_to_bits(ref_mask, tk))
             ref_mask = ref.mask_next
-        log(f"  [{label}] step {t}: log_eps={le} skipped(next)={mask_to_bits(ref_mask, tk).mean():.3f}")
+        sk = mask_to_bits(ref_mask, tk)
+        sk = sk[sel].mean() if sel is not None else sk.mean()
+        log(f"  [{label}] step {t}: log_eps={le:.4g} skipped(next, compared rows)={sk:.3f} "
+            f"mismatches beyond band={per_step[0]} near-threshold={per_step[1]} "
+            f"(differing {per_step[2]}) max|d| so far={cmp.max_abs:.2e}")
     cmp.check(label)
     return cmp, ref_mask

@@ -158,3 +158,29 @@ def test_error_budget_schedule():
         tsa.ErrorBudgetSchedule([-8, -10])       # tightens later
     with pytest.raises(ValueError):
         tsa.ErrorBudgetSchedule([0.5])
+
+
+def test_create_rejects_strides_that_overlap_out_rows():
+    """out is written through the strides it shares with q, k and v: a stride set under which two
+    (b, h, n) rows land on the same memory would be a silent write race."""
+    B, H, N, D = 2, 3, 1000, 64
+    mk = lambda strides, b=B, h=H: (lambda: tsa.lite_attn_create(b, h, N, D, tile_q=64,
+                                                                  strides=strides))
+    assert _status(mk((H * N * D, N * D, D))) == binding.OK                  # contiguous
+    assert _status(mk((H * N * 3 * D, N * 3 * D, 3 * D))) == binding.OK      # packed QKV view
+    assert _status(mk((N * H * D, D, H * D))) == binding.OK                  # [B][N][H][D]
+    assert _status(mk((0, N * D, D))) == binding.ERR_INVALID_ARG             # batches share rows
+    assert _status(mk((H * N * D, 0, D))) == binding.ERR_INVALID_ARG         # heads share rows
+    assert _status(mk((H * N * D, N * D - 8, D))) == binding.ERR_INVALID_ARG  # heads overlap
+    assert _status(mk((N * D, N * D, D))) == binding.ERR_INVALID_ARG         # b and h collide
+    assert _status(mk((0, 0, D), b=1, h=1)) == binding.OK                    # one head: no overlap
+    assert _status(mk((8, 0, D), b=1, h=1)) == binding.OK
+
+
+def test_last_launch_before_any_step():
+    import threading
+    got = []
+    th = threading.Thread(target=lambda: got.append(tsa.lite_attn_last_launch()))
+    th.start()
+    th.join()
+    assert got == [(0, -1)]

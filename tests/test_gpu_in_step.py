@@ -53,9 +53,10 @@ def test_in_step_full_size_sampled_parity():
     dev = device()
     cfg = get_config(3)
     rows = _sample_rows(cfg, np.random.default_rng(33), n_heads=2, per_head=2)
-    log(f"== in-step {cfg.name} full size, {len(rows)} sampled query tiles")
+    log(f"== in-step {cfg.name} full size, {len(rows)} sampled query tiles, {cfg.steps} steps")
     wl = Workload(cfg, dev)
-    teacher_forced_chain(cfg, wl, 3, rows=rows, label="ins-" + cfg.name, in_step_skip=True)
+    teacher_forced_chain(cfg, wl, cfg.steps, rows=rows, label="ins-" + cfg.name,
+                         in_step_skip=True)
     wl.drop_cache()
     torch.cuda.empty_cache()
 

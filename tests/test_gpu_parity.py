@@ -79,7 +79,9 @@ def _sample_rows(cfg, rng, n_heads, per_head):
     return sorted(rows)
 
 
-FULL = [(2, 3), (3, 3), (4, 3), (5, 6)]
+# Every step of every schedule: the late steps run at the loosest budgets with most tiles
+# skipped, and they are most of what the benchmark times.
+FULL = [(2, 10), (3, 10), (4, 10), (5, 20)]
 
 
 @pytest.mark.parametrize("cid,steps", FULL, ids=[f"config{c}" for c, _ in FULL])
@@ -90,6 +92,24 @@ def test_full_size_sampled_parity(cid, steps):
     rows = _sample_rows(cfg, rng, n_heads=2, per_head=2)
     log(f"== {cfg.name} full size N={cfg.seq_len}, {len(rows)} sampled query tiles, {steps} steps")
     wl = Workload(cfg, dev)
+    assert steps == cfg.steps
     teacher_forced_chain(cfg, wl, steps, rows=rows, label=cfg.name)
+    wl.drop_cache()
+    torch.cuda.empty_cache()
+
+
+def test_full_size_scheduled_parity_with_dense_prefix():
+    """lite_attn_step_scheduled (heaviest-first order from the visit counts, caller workspace)
+    against the oracle over the whole HunyuanVideo-shaped schedule, on sampled query tiles that
+    include the dense-prefix rows, which the schedule moves to the front."""
+    dev = device()
+    cfg = get_config(4)
+    rows = _sample_rows(cfg, np.random.default_rng(44), n_heads=2, per_head=2)
+    rows = sorted(set(rows) | {(0, h, i) for h in (0, cfg.heads - 1) for i in (0, 1, 2)})
+    log(f"== scheduled {cfg.name} full size, {len(rows)} sampled query tiles, {cfg.steps} steps")
+    wl = Workload(cfg, dev)
+    att = make_attention(cfg)
+    teacher_forced_chain(cfg, wl, cfg.steps, rows=rows, att=att, label="sched-" + cfg.name,
+                         workspace=att.new_workspace(dev))
     wl.drop_cache()
     torch.cuda.empty_cache()

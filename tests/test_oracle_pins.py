@@ -444,3 +444,45 @@ def test_refresh_clears_a_row_when_the_attention_moves_into_skipped_tiles():
                               step=1, tile_stats=r0.stats_next, refresh_delta=1e6, **kw)
     assert not keep.refreshed.any()
     assert np.array_equal(keep.mask_next, keep.mask_next | r0.mask_next)   # bits only grow
+
+
+# ------------------------------------------------------------------ the chain driver
+@pytest.mark.parametrize("order", ["asc", "alt"])
+def test_run_chain_ref_matches_a_brute_force_chain(order):
+    """run_chain_ref against a chain built by hand from the pure-Python pieces: every step
+    starts from the previous step's mask (step 0 from an empty one), the mask it yields is the
+    mask at the start of the step, flags follow the brute-force rule in this step's traversal
+    direction, and the output is block-masked attention over that start mask."""
+    from oracle import run_chain_ref
+    rng = np.random.default_rng(77)
+    n, d, tq, tk, steps, scale = 23, 3, 4, 3, 5, 1.0
+    eps = [-math.inf, -1.0, -1.5, -0.8, -0.8]
+    base_q, base_k = rng.standard_normal((n, d)) * 2.0, rng.standard_normal((n, d)) * 2.0
+    v = rng.standard_normal((n, 2))
+    xs = [(base_q + 0.1 * rng.standard_normal((n, d)), base_k + 0.1 * rng.standard_normal((n, d)))
+          for _ in range(steps)]
+    inputs = lambda t: (_one_head(xs[t][0]), _one_head(xs[t][1]), _one_head(v))
+    tqn, tkn, _ = mask_geometry(n, tq, tk)
+    skipped = [[False] * tkn for _ in range(tqn)]     # the hand-built chain's mask
+    seen = 0
+    for t, start, res in run_chain_ref(inputs, steps, eps, batch=1, heads=1, seq_len=n,
+                                       tile_q=tq, tile_k=tk, softmax_scale=scale, order=order):
+        assert t == seen
+        seen += 1
+        assert mask_to_bits(start, tkn)[0, 0].tolist() == skipped, t
+        q, k = xs[t][0].tolist(), xs[t][1].tolist()
+        descending = order == "alt" and t % 2 == 1
+        flags, margins = pyref.brute_flags(q, k, skipped, tq, tk, scale, eps[t], descending)
+        allowed = [[not skipped[r // tq][c // tk] for c in range(n)] for r in range(n)]
+        want = pyref.masked_attention(q, k, v.tolist(), allowed, scale)
+        np.testing.assert_allclose(res.out[0, 0], np.array(want), rtol=1e-12, atol=1e-12)
+        got = mask_to_bits(res.mask_next, tkn)[0, 0]
+        for i in range(tqn):
+            for j in range(tkn):
+                if skipped[i][j]:
+                    assert got[i, j]
+                elif abs(margins[i][j]) > 1e-9:
+                    assert bool(got[i, j]) == flags[i][j], (t, i, j)
+        skipped = [[bool(x) for x in row] for row in got]
+    assert seen == steps
+    assert sum(map(sum, skipped)) > 0          # the chain flags something
