@@ -202,6 +202,22 @@ int lite_attn_step_scheduled(lite_attn_t handle, const void* q, const void* k, c
                              void* out, uint32_t* mask, float log_eps_t, int32_t step,
                              void* workspace, void* stream);
 
+/* lite_attn_step_scheduled without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments as lite_attn_step_scheduled less `workspace`, same results bit
+ * for bit. The workspace is a 1 MiB array in the library's static device memory, one per
+ * device, held until the process ends; this call allocates nothing. It holds the schedule of
+ * up to about 174,000 query tiles (B * H * ceil(N / tile_q)); larger problems return
+ * UNSUPPORTED (lite_attn_workspace_bytes(handle) > 1 MiB) without any device call. The array's
+ * address is looked up on the first call on each device, with that device current. Every call
+ * on a device shares the one array and leaves its contents behind (nothing in it needs to
+ * start at zero): calls that overlap on one device race, so order them, for example on one
+ * stream. `stream` must belong to the current device (INVALID_ARG otherwise). Returns what
+ * lite_attn_step_scheduled returns, and HIP when the array's address cannot be taken. */
+int lite_attn_step_scheduled_static(lite_attn_t handle, const void* q, const void* k,
+                                    const void* v, void* out, uint32_t* mask, float log_eps_t,
+                                    int32_t step, void* stream);
+
 /* Clear every word of `mask` (a new generation starts dense). LiteAttention, page 1
  * "Architecture Overview": decisions persist until the attention distribution shifts; this
  * is the explicit way to drop them. Uses a fill kernel (no memset node), so it may be

@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     lite_attn_step,
     lite_attn_step_refresh,
     lite_attn_step_scheduled,
+    lite_attn_step_scheduled_static,
     lite_attn_workspace_bytes,
     make_config,
 )

@@ -30,6 +30,7 @@ EXPORTS = (
     "lite_attn_step_refresh",
     "lite_attn_workspace_bytes",
     "lite_attn_step_scheduled",
+    "lite_attn_step_scheduled_static",
     "lite_attn_reset_mask",
     "lite_attn_mask_popcount",
     "lite_attn_status_string",
@@ -113,6 +114,9 @@ def _load() -> ctypes.CDLL:
     lib.lite_attn_step_scheduled.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
                                              vp, vp]
     lib.lite_attn_step_scheduled.restype = ctypes.c_int
+    lib.lite_attn_step_scheduled_static.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                                    ctypes.c_int32, vp]
+    lib.lite_attn_step_scheduled_static.restype = ctypes.c_int
     lib.lite_attn_reset_mask.argtypes = [vp, vp, vp]
     lib.lite_attn_reset_mask.restype = ctypes.c_int
     lib.lite_attn_mask_popcount.argtypes = [vp, vp, vp, vp]
@@ -345,6 +349,21 @@ def lite_attn_step_scheduled(handle: Handle, q, k, v, out, mask, log_eps_t: floa
                                          ctypes.c_int32(step), _ptr(workspace, "workspace", dev),
                                          ctypes.c_void_p(st)),
            "lite_attn_step_scheduled")
+
+
+def lite_attn_step_scheduled_static(handle: Handle, q, k, v, out, mask, log_eps_t: float,
+                                    step: int, stream=None):
+    """lite_attn_step_scheduled with the library's static workspace (allocates nothing)."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _check_qkvo(handle, t, name)
+    _check_mask(handle, mask)
+    dev = None if isinstance(q, int) else q.device
+    st = _stream_ptr(stream, dev)
+    _check(_lib.lite_attn_step_scheduled_static(handle.ptr, _ptr(q, "q", dev), _ptr(k, "k", dev),
+                                                _ptr(v, "v", dev), _ptr(out, "out", dev),
+                                                _ptr(mask, "mask", dev), ctypes.c_float(log_eps_t),
+                                                ctypes.c_int32(step), ctypes.c_void_p(st)),
+           "lite_attn_step_scheduled_static")
 
 
 def lite_attn_reset_mask(handle: Handle, mask, stream=None):

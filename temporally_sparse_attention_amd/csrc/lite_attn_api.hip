@@ -1,6 +1,7 @@
 // C ABI of the LiteAttention step library (declared in include/lite_attn.h): argument
 // validation, error reporting and kernel dispatch. No device memory is allocated here (the
-// persistent launches' tile queues are static device memory of the library).
+// persistent launches' tile queues and the workspace of lite_attn_step_scheduled_static are
+// static device memory of the library).
 
 #include <hip/hip_runtime.h>
 
@@ -142,6 +143,44 @@ bool strides_one_to_one(int64_t B, int64_t H, int64_t N, int64_t D, int64_t sb, 
     if ((__int128)live[i].stride < span) return false;
   }
   return true;
+}
+
+// Workspace of lite_attn_step_scheduled_static, for callers that cannot allocate: file-scope
+// device memory, one copy per device, held until the process ends. Host code never uses this
+// name as an address: the device address is taken once per device, with that device current,
+// and passed to the kernels like a caller's workspace. Every call on a device shares the one
+// array, so calls that overlap on a device race.
+constexpr size_t kStaticWorkspaceBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+struct ScratchTable {
+  std::mutex mu;
+  std::map<int, void*> ptr;   // device -> address of its copy of `scratch`
+};
+
+ScratchTable& scratch_table() {
+  static ScratchTable* t = new ScratchTable;   // never destroyed: usable during static teardown
+  return *t;
+}
+
+// Device address of `scratch` on the current device (taken on the first call per device).
+hipError_t static_workspace(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  ScratchTable& t = scratch_table();
+  std::lock_guard<std::mutex> lock(t.mu);
+  auto it = t.ptr.find(dev);
+  if (it == t.ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    it = t.ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -371,6 +410,41 @@ int lite_attn_step_scheduled(lite_attn_t h, const void* q, const void* k, const 
                              void* workspace, void* stream) {
   return step_impl("step_scheduled", h, q, k, v, out, mask, log_eps_t, step, workspace, true,
                    nullptr, 0.f, false, stream);
+}
+
+int lite_attn_step_scheduled_static(lite_attn_t h, const void* q, const void* k,
+                                    const void* v, void* out, uint32_t* mask, float log_eps_t,
+                                    int32_t step, void* stream) {
+  static const char* who = "step_scheduled_static";
+  try {
+    if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL handle", who);
+    const size_t need = lite_attn_workspace_bytes(h);
+    if (need > kStaticWorkspaceBytes)
+      return fail(LITE_ATTN_ERR_UNSUPPORTED,
+                  "%s: the schedule needs %zu bytes of workspace (%lld query tiles); the static "
+                  "workspace holds %zu: use lite_attn_step_scheduled with a caller workspace",
+                  who, need, (long long)h->cfg.batch * h->cfg.heads * h->Tq,
+                  kStaticWorkspaceBytes);
+    if ((int64_t)h->cfg.batch * h->cfg.heads * h->cfg.seq_len == 0) return LITE_ATTN_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (st != nullptr && st != hipStreamPerThread) {
+      int cur = -1, dev = -2;
+      if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(st, &dev) != hipSuccess ||
+          dev != cur)
+        return fail(LITE_ATTN_ERR_INVALID_ARG,
+                    "%s: the stream must belong to the current device (the static workspace "
+                    "used is the current device's)", who);
+    }
+    void* ws = nullptr;
+    const hipError_t e = static_workspace(&ws);
+    if (e != hipSuccess)
+      return fail(LITE_ATTN_ERR_HIP, "%s: static workspace address: %s", who,
+                  hipGetErrorString(e));
+    return step_impl(who, h, q, k, v, out, mask, log_eps_t, step, ws, true, nullptr, 0.f, false,
+                     stream);
+  } catch (...) {
+    return fail(LITE_ATTN_ERR_HIP, "%s: unexpected exception", who);
+  }
 }
 
 int lite_attn_reset_mask(lite_attn_t h, uint32_t* mask, void* stream) {

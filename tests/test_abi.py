@@ -184,3 +184,22 @@ def test_last_launch_before_any_step():
     th.start()
     th.join()
     assert got == [(0, -1)]
+
+
+def test_static_workspace_entry_point_rejects_large_problems_without_a_device_call():
+    lib = binding.library()
+    p = ctypes.c_void_p(4096)
+    small = tsa.lite_attn_create(1, 2, 1000, 128)
+    assert tsa.lite_attn_workspace_bytes(small) <= 1 << 20
+    big = tsa.lite_attn_create(200, 8, 131072, 64, tile_q=128)      # 1.6M query tiles
+    assert tsa.lite_attn_workspace_bytes(big) > 1 << 20
+    st = lambda h, eps=-1.0: lib.lite_attn_step_scheduled_static(h.ptr, p, p, p,
+                                                                 ctypes.c_void_p(8192), p,
+                                                                 ctypes.c_float(eps), 0, None)
+    assert st(big) == binding.ERR_UNSUPPORTED
+    assert "static workspace" in tsa.lite_attn_last_error()
+    assert lib.lite_attn_step_scheduled_static(None, p, p, p, p, p, ctypes.c_float(-1.0), 0,
+                                               None) == binding.ERR_INVALID_ARG
+    empty = tsa.lite_attn_create(1, 0, 100, 64, tile_q=64)
+    assert lib.lite_attn_step_scheduled_static(empty.ptr, None, None, None, None, None,
+                                               ctypes.c_float(-1.0), 0, None) == binding.OK
