@@ -116,8 +116,9 @@ typedef struct lite_attn_s* lite_attn_t;
  * are not multiples of 8 elements, strides under which two (b, h, n) rows of out would overlap
  * (out is written through the shared strides), dense_prefix outside [0, seq_len], unknown
  * option bits or a nonzero reserved field; UNSUPPORTED for a
- * head_dim / tile / dtype combination without a kernel or for Tk > 2048 (N > 131072 with
- * 64-key tiles). On failure *out is set to NULL. */
+ * head_dim / tile / dtype combination without a kernel, for Tk > 2048 (N > 131072 with
+ * 64-key tiles), and, for bf16, when one head's rows span 2^31 bytes or more
+ * ((N - 1) * stride_n * 2 + head_dim * 2). On failure *out is set to NULL. */
 int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out);
 
 /* Release a handle. NULL is accepted. Returns OK. */

@@ -259,6 +259,13 @@ int lite_attn_create(const lite_attn_config* cfg, lite_attn_t* out) {
                   "create: no kernel for dtype=%d head_dim=%d tile_q=%d (built: head_dim 64/128,"
                   " tile_q 64/128, tile_k 64)",
                   c.dtype, c.head_dim, c.tile_q);
+    // The bf16 kernels address one head's K and V rows through a 32-bit buffer offset.
+    if (c.dtype == LITE_ATTN_BF16 && c.seq_len > 0 &&
+        ((int64_t)c.seq_len - 1) * sn * 2 + (int64_t)c.head_dim * 2 >= (int64_t(1) << 31))
+      return fail(LITE_ATTN_ERR_UNSUPPORTED,
+                  "create: one head spans %lld bytes with stride_n %lld; the bf16 kernels "
+                  "need it below 2^31",
+                  (long long)(((int64_t)c.seq_len - 1) * sn * 2 + c.head_dim * 2), (long long)sn);
     const int64_t tq = ceil_div(c.seq_len, c.tile_q);
     const int64_t tk = ceil_div(c.seq_len, c.tile_k);
     if (tk > lite_attn::kMaxTilesK)

@@ -90,19 +90,29 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Turn mask row `mrow` (W words) into the list of key tiles to visit, in traversal order.
-// Runs on wave 0 (each lane owns words 2*lane and 2*lane+1, W <= 128); also clears the keep
-// bitset. Ends with a workgroup barrier; returns the list length.
+// Wave 0's share of a mask row: lane l holds words 2l and 2l+1 (clamped into the row, W >= 1,
+// so that both loads are always in flight together; W <= 128). Other waves load nothing.
+__device__ __forceinline__ void load_mask_words(const uint32_t* mrow, int W, uint32_t& r0,
+                                                uint32_t& r1) {
+  if (threadIdx.x < 64) {
+    r0 = mrow[min(2 * (int)threadIdx.x, W - 1)];
+    r1 = mrow[min(2 * (int)threadIdx.x + 1, W - 1)];
+  }
+}
+
+// Turn a mask row (its words as load_mask_words holds them) into the list of key tiles to
+// visit, in traversal order. Runs on wave 0, which also keeps the row's words in `old` for the
+// mask update at the end of the tile; every thread clears the keep bitset. Ends with a
+// workgroup barrier; returns the list length.
 template <int NT>
-__device__ int build_visit_list(const uint32_t* mrow, int W, int Tk, bool descending,
-                                uint16_t* list, uint32_t* keep, int* s_count) {
+__device__ int build_visit_list(uint32_t r0, uint32_t r1, int W, int Tk, bool descending,
+                                uint16_t* list, uint32_t* keep, uint32_t* old, int* s_count) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
     const int w0 = 2 * lane, w1 = 2 * lane + 1;
-    // both words are loaded unconditionally (the index is clamped to the row, W >= 1), so the
-    // two loads are in flight together
-    const uint32_t r0 = mrow[min(w0, W - 1)], r1 = mrow[min(w1, W - 1)];
+    if (w0 < W) old[w0] = r0;
+    if (w1 < W) old[w1] = r1;
     uint32_t b0 = w0 < W ? (~r0 & valid_bits(w0, Tk)) : 0u;
     uint32_t b1 = w1 < W ? (~r1 & valid_bits(w1, Tk)) : 0u;
     const int cnt = __popc(b0) + __popc(b1);
@@ -133,16 +143,16 @@ __device__ int build_visit_list(const uint32_t* mrow, int W, int Tk, bool descen
   return *s_count;
 }
 
-// Fold this step's flags into the mask row: flags = visited & ~keep & ~exempt.
+// Fold this step's flags into the mask row: flags = visited & ~keep & ~exempt. `old` holds the
+// row as it was at the start of the tile (only this workgroup writes the row).
 template <int NT>
-__device__ void write_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* keep,
-                               bool row_exempt, int exempt_cols) {
+__device__ void write_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* old,
+                               const uint32_t* keep, bool row_exempt, int exempt_cols) {
   if (row_exempt) return;
   for (int w = threadIdx.x; w < W; w += NT) {
-    const uint32_t old = mrow[w];
-    const uint32_t visited = ~old & valid_bits(w, Tk);
+    const uint32_t visited = ~old[w] & valid_bits(w, Tk);
     const uint32_t flags = visited & ~keep[w] & ~low_bits(w, exempt_cols);
-    if (flags) mrow[w] = old | flags;
+    if (flags) mrow[w] = old[w] | flags;
   }
 }
 
@@ -186,8 +196,8 @@ __device__ bool refresh_decision(float m_run, bool row_valid, int valid_rows, fl
 
 // Clears the valid bits of a mask row (reserved bits stay as they are: zero).
 template <int NT>
-__device__ void clear_mask_row(uint32_t* mrow, int W, int Tk) {
-  for (int w = threadIdx.x; w < W; w += NT) mrow[w] &= ~valid_bits(w, Tk);
+__device__ void clear_mask_row(uint32_t* mrow, int W, int Tk, const uint32_t* old) {
+  for (int w = threadIdx.x; w < W; w += NT) mrow[w] = old[w] & ~valid_bits(w, Tk);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -263,13 +273,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // keeps the many loop-invariant addresses out of scalar registers. The instruction has no
 // register result, and M0 is declared clobbered.
 __device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_a, uint32_t lds_b,
-                                          uint32_t voff) {
+                                          uint32_t voff, uint32_t soff) {
   asm volatile(
       "s_add_u32 m0, %0, %1\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds"
       :
-      : "s"(lds_a), "s"(lds_b), "v"(voff), "s"(rsrc)
+      : "s"(lds_a), "s"(lds_b), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory", "m0", "scc");
 }
 
@@ -281,11 +291,70 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
 // The launch parameters as the kernel received them, read through scalar loads.
 typedef const FwdParams __attribute__((address_space(4))) ArgParams;
 
+// Tile position of queue entry w (persistent launches without a schedule). The dense-prefix
+// query tiles (P per head) never skip: they are the longest, and go first, head by head, so
+// that none of them starts last. The other tiles follow in the direction of the step's key
+// traversal (measured: +3% on a descending step with 39% of tiles skipped, neutral elsewhere).
+// With a schedule, the entry is the position in the schedule.
+template <int NW>
+__device__ __forceinline__ uint32_t queue_position(ArgParams& p, uint32_t w) {
+  if (p.perm != nullptr) return w;
+  const uint32_t n_tiles = (uint32_t)(p.B * p.H * p.Tq);
+  const uint32_t Tq = (uint32_t)p.Tq;
+  const uint32_t P = min(Tq, (uint32_t)((p.dense_prefix + NW * 32 - 1) / (NW * 32)));
+  const uint32_t n_pre = (uint32_t)(p.B * p.H) * P;
+  if (w < n_pre) return (w / P) * Tq + w % P;
+  uint32_t r = w - n_pre;                        // among the B*H*(Tq-P) other tiles
+  if (p.descending) r = n_tiles - n_pre - 1u - r;
+  return (r / (Tq - P)) * Tq + P + r % (Tq - P);
+}
+
+// What a query tile needs before its first K/V load: the wave's Q rows as MFMA B operands
+// (lane holds features 16c + 8*half .. +7 of query row l32, for every 16-feature step c) and,
+// on wave 0, its share of the tile's mask row; both are loaded together, so that the two
+// memory latencies overlap.
+template <int D>
+struct TileInputs {
+  bf16x8 qf[D / 16];
+  uint32_t m0, m1;
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void load_tile_inputs(ArgParams& p, uint32_t pos, TileInputs<D>& in) {
+  const uint32_t tile = p.perm ? p.perm[pos] : pos;
+  const int i = (int)(tile % (uint32_t)p.Tq);
+  const int bh = (int)(tile / (uint32_t)p.Tq);
+  const int b = bh / p.H, h = bh % p.H;
+  const __bf16* qh = static_cast<const __bf16*>(p.q) + (int64_t)b * p.sb + (int64_t)h * p.sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);
+  const int qrow = i * NW * 32 + wave * 32 + (lane & 31);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (qrow < p.N) {
+      in.qf[c] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * p.sn + 16 * c +
+                                                  8 * (lane >> 5));
+    } else {
+      in.qf[c] = bf16x8{};
+    }
+  }
+  load_mask_words(p.mask + (size_t)tile * p.W, p.W, in.m0, in.m1);
+}
+
 // One query tile. `args` is the address of the kernel's argument segment (the FwdParams), `w_in`
-// the tile's position (in the schedule when there is one). Inlined into the two out-of-line
-// drivers below, which the kernel calls.
+// the tile's position (in the schedule when there is one), `in` its inputs, already loaded.
+// Inlined into the out-of-line drivers below, which the kernel calls (one instantiation per
+// configuration, so both drivers share its LDS arrays; s_next is a constant at each call site).
+// With s_next (persistent launches), thread 0 takes the next queue entry when the tile loop
+// ends and publishes it through *s_next; the tile returns that entry, the same value in every
+// thread (>= B*H*Tq: the queue is empty). Without it, returns 0. Measured alternatives: taking
+// the entry when the tile starts was 3-5% slower on sparse steps (a reserved tile waits for its
+// workgroup while others go idle), and loading the next tile's Q rows before this tile's
+// epilogue was 7-9% slower (Q registers carried from one tile to the next cost the tile loop
+// its pinned MFMA/VALU interleave).
 template <int D, int NW, bool INSTEP>
-__device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
+__device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
+                                                   TileInputs<D>& in, uint32_t* s_next) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t a_lo = __builtin_amdgcn_readfirstlane((uint32_t)args);
   const uint32_t a_hi = __builtin_amdgcn_readfirstlane((uint32_t)(args >> 32));
@@ -305,6 +374,7 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
   __shared__ uint16_t s_list[kMaxTilesK + 8];   // +8: the loop reads a few entries ahead
   __shared__ uint32_t s_keep[kMaxWords];
   __shared__ uint64_t s_wkeep[NW][kMaxTilesK / 64];   // per-wave keep votes by list position
+  __shared__ uint32_t s_old[kMaxWords];                // the mask row at the start of the tile
   __shared__ int s_count;
 
   const int tid = threadIdx.x;
@@ -319,7 +389,6 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
   const int bh = (int)(tile / (uint32_t)p.Tq);
   const int b = bh / p.H, h = bh % p.H;
   const int64_t head_off = (int64_t)b * p.sb + (int64_t)h * p.sh;
-  const __bf16* __restrict__ qh = static_cast<const __bf16*>(p.q) + head_off;
   const __bf16* __restrict__ kh = static_cast<const __bf16*>(p.k) + head_off;
   const __bf16* __restrict__ vh = static_cast<const __bf16*>(p.v) + head_off;
   __bf16* __restrict__ oh = static_cast<__bf16*>(p.out) + head_off;
@@ -328,23 +397,12 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
   const int64_t sn = p.sn;
   const uint32_t row_bytes = (uint32_t)sn * 2u;
 
-  // Q rows of this wave as MFMA B operands: lane holds features 16c + 8*half .. +7 of query
-  // row l32, for every 16-feature step c. Loaded before the visiting list is built, so that
-  // the two memory latencies overlap.
   const int qrow = i * BQ + wave * 32 + l32;
   const bool row_valid = qrow < N;
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (row_valid) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(qh + (int64_t)qrow * sn + 16 * c + 8 * half);
-    } else {
-      qf[c] = bf16x8{};
-    }
-  }
+  bf16x8 (&qf)[D / 16] = in.qf;
 
-  const int cnt = build_visit_list<NT>(mrow, p.W, p.Tk, p.descending != 0, s_list, s_keep,
-                                       &s_count);
+  const int cnt = build_visit_list<NT>(in.m0, in.m1, p.W, p.Tk, p.descending != 0, s_list,
+                                       s_keep, s_old, &s_count);
 
   // Consume Q here: the compiler then waits for these loads once, before the tile loop, rather
   // than at the loop's first MFMA on every iteration (where the wait would also cover the K/V
@@ -371,27 +429,29 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
     voff[n] = ch < G::CH ? (uint32_t)row * row_bytes + 16u * ch : kOobOffset;
   }
   const uint32_t wave1k = 1024u * wave;   // this wave's first 1 KB slot of a stage
-  auto tile_bytes = [&](int key0) {
-    return (uint32_t)(min(BK, N - key0) - 1) * row_bytes + D * 2;
-  };
+  // One buffer resource per tensor covers the head's N rows, built once per query tile: rows
+  // >= N of the ragged last tile lie past its end and read as zeros, and a tile load only adds
+  // the tile's first row as a scalar offset (the head's span is below 2^31 bytes, checked when
+  // the handle is created, so no offset wraps).
+  const uint32_t head_bytes = (uint32_t)(N - 1) * row_bytes + D * 2;
+  const i32x4 rk = make_rsrc(kh, head_bytes);
+  const i32x4 rv = make_rsrc(vh, head_bytes);
   auto issue_k = [&](int j, unsigned char* dst) {
-    const int key0 = j * BK;
-    const i32x4 r = make_rsrc(kh + (int64_t)key0 * sn, tile_bytes(key0));
+    const uint32_t soff = (uint32_t)(j * BK) * row_bytes;
     const uint32_t base = lds_address(dst);
 #pragma unroll
     for (int n = 0; n < KLOADS; ++n) {
       const int x = wave + NW * n;
-      if (KLOADS * NW == G::KCH || x < G::KCH) lds_dma16(r, wave1k, base + NW * n * 1024, koff[n]);
+      if (KLOADS * NW == G::KCH || x < G::KCH) lds_dma16(rk, wave1k, base + NW * n * 1024, koff[n], soff);
     }
   };
   auto issue_v = [&](int j, unsigned char* dst) {
-    const int key0 = j * BK;
-    const i32x4 r = make_rsrc(vh + (int64_t)key0 * sn, tile_bytes(key0));
+    const uint32_t soff = (uint32_t)(j * BK) * row_bytes;
     const uint32_t base = lds_address(dst);
 #pragma unroll
     for (int n = 0; n < VLOADS; ++n) {
       const int x = wave + NW * n;
-      if (VLOADS * NW == G::VCH || x < G::VCH) lds_dma16(r, wave1k, base + NW * n * 1024, voff[n]);
+      if (VLOADS * NW == G::VCH || x < G::VCH) lds_dma16(rv, wave1k, base + NW * n * 1024, voff[n], soff);
     }
   };
 
@@ -703,6 +763,11 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
       jv3 = jv5;
     }
   }
+  // The next queue entry is taken as the tile loop ends: its latency overlaps the epilogue, and
+  // the queue still hands each tile to the first workgroup that is nearly free.
+  uint32_t next = 0u;
+  if (s_next != nullptr && threadIdx.x == 0)
+    next = __hip_atomic_fetch_add(&p.queue[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if constexpr (!INSTEP) {
     // a visited tile is kept when any wave voted keep at its list position
@@ -741,8 +806,14 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
     clear = refresh_decision<NW>(m_run, row_valid, min(BQ, N - i * BQ), p.scale,
                                  p.refresh_delta, p.stats + tile, s_part, &s_clear);
   }
-  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk);
-  else write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, row_exempt, exempt_cols);
+  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk, s_old);
+  else write_mask_row<NT>(mrow, p.W, p.Tk, s_old, s_keep, row_exempt, exempt_cols);
+  if (s_next == nullptr) return 0u;
+  if (threadIdx.x == 0) *s_next = next;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s_next);
+#else
+  return 0u;
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -753,21 +824,53 @@ __device__ __forceinline__ void bf16_tile_body(uint64_t args, uint32_t w_in) {
 // One tile at position w_in (one workgroup per tile).
 template <int D, int NW, bool INSTEP>
 __device__ __attribute__((noinline)) void bf16_tile(uint64_t args, uint32_t w_in) {
-  bf16_tile_body<D, NW, INSTEP>(args, w_in);
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)args);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(args >> 32));
+  ArgParams& p = *(ArgParams*)(((uint64_t)hi << 32) | lo);
+  TileInputs<D> in;
+  load_tile_inputs<D, NW>(p, __builtin_amdgcn_readfirstlane(w_in), in);
+  bf16_tile_body<D, NW, INSTEP>(args, w_in, in, nullptr);
+#endif
 }
 
 // Tiles from the queue until it runs out. The loop lives inside the out-of-line function, so the
 // callee-saved registers are saved and restored once per workgroup rather than once per tile
 // (which cost about 8 us per tile, 38% of the cost of a tile with one key tile to visit). The
 // argument address passes through an empty asm at the top of every iteration, so that nothing
-// loaded through it is held in registers from one tile to the next.
-//
-// Order without a schedule. The dense-prefix query tiles (P per head) never skip: they are the
-// longest, and go first, head by head, so that none of them starts last. The other tiles follow
-// in the direction of the step's key traversal (measured: +3% on a descending step with 39% of
-// tiles skipped, neutral elsewhere).
+// loaded through it is held in registers from one tile to the next. Each tile takes the next
+// queue entry while it runs (queue_position gives the order).
 template <int D, int NW, bool INSTEP>
 __device__ __attribute__((noinline)) void bf16_tiles(uint64_t args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ uint32_t s_next;
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)args);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(args >> 32));
+  {
+    ArgParams& p = *(ArgParams*)(((uint64_t)hi << 32) | lo);
+    if (threadIdx.x == 0)
+      s_next = __hip_atomic_fetch_add(&p.queue[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+  uint32_t w = __builtin_amdgcn_readfirstlane(s_next);
+  for (;;) {
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    ArgParams& p = *(ArgParams*)(((uint64_t)hi << 32) | lo);
+    if (w >= (uint32_t)(p.B * p.H * p.Tq)) break;   // the same value in every thread
+    const uint32_t pos = queue_position<NW>(p, w);
+    TileInputs<D> in;
+    load_tile_inputs<D, NW>(p, pos, in);
+    w = bf16_tile_body<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos, in, &s_next);
+    __syncthreads();           // LDS and s_next are reused by the next tile
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// At D = 128 and tile_q 64 the tile runs one wave per SIMD at 256 VGPRs; inlined into the queue
+// loop it lost its pinned MFMA/VALU interleave, so that configuration calls the one-tile driver
+// once per tile, with no prefetch.
+template <int D, int NW, bool INSTEP>
+__device__ __attribute__((noinline)) void bf16_tiles_calls(uint64_t args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ uint32_t s_next;
   for (;;) {
@@ -779,25 +882,8 @@ __device__ __attribute__((noinline)) void bf16_tiles(uint64_t args) {
       s_next = __hip_atomic_fetch_add(&p.queue[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const uint32_t w = s_next;
-    const uint32_t n_tiles = (uint32_t)(p.B * p.H * p.Tq);
-    if (w >= n_tiles) break;   // the same value in every thread
-    const uint32_t Tq = (uint32_t)p.Tq;
-    const uint32_t P = min(Tq, (uint32_t)((p.dense_prefix + NW * 32 - 1) / (NW * 32)));
-    const uint32_t n_pre = (uint32_t)(p.B * p.H) * P;
-    uint32_t pos = w;          // with a schedule: its position
-    if (p.perm == nullptr) {
-      if (w < n_pre) {
-        pos = (w / P) * Tq + w % P;
-      } else {
-        uint32_t r = w - n_pre;                        // among the B*H*(Tq-P) other tiles
-        if (p.descending) r = n_tiles - n_pre - 1u - r;
-        pos = (r / (Tq - P)) * Tq + P + r % (Tq - P);
-      }
-    }
-    // At D = 128 and tile_q 64 the tile runs one wave per SIMD at 256 VGPRs; inlined into this
-    // loop it lost its pinned MFMA/VALU interleave, so there it is called once per tile.
-    if constexpr (D == 128 && NW == 2) bf16_tile<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos);
-    else bf16_tile_body<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, pos);
+    if (w >= (uint32_t)(p.B * p.H * p.Tq)) break;   // the same value in every thread
+    bf16_tile<D, NW, INSTEP>(((uint64_t)hi << 32) | lo, queue_position<NW>(p, w));
     __syncthreads();           // LDS and s_next are reused by the next tile
   }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -817,7 +903,8 @@ __global__ void __launch_bounds__(NW * 64, 2) lite_attn_fwd_bf16(FwdParams p) {
     bf16_tile<D, NW, INSTEP>(args, blockIdx.x);
     return;
   }
-  bf16_tiles<D, NW, INSTEP>(args);
+  if constexpr (D == 128 && NW == 2) bf16_tiles_calls<D, NW, INSTEP>(args);
+  else bf16_tiles<D, NW, INSTEP>(args);
   // Every workgroup has taken its last position before it counts itself finished, so the last
   // one to finish can reset the queue.
   if (threadIdx.x == 0) {
@@ -866,8 +953,11 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
   const int N = p.N;
   const int64_t sn = p.sn;
 
-  const int cnt = build_visit_list<NT>(mrow, p.W, p.Tk, p.descending != 0, s_list, s_keep,
-                                       &s_count);
+  __shared__ uint32_t s_old[kMaxWords];
+  uint32_t r0 = 0u, r1 = 0u;
+  load_mask_words(mrow, p.W, r0, r1);
+  const int cnt = build_visit_list<NT>(r0, r1, p.W, p.Tk, p.descending != 0, s_list, s_keep,
+                                       s_old, &s_count);
 
   const int qrow = i * BQ + wave * 32 + l32;
   const bool row_valid = qrow < N;
@@ -996,8 +1086,8 @@ __global__ void __launch_bounds__(NW * 64) lite_attn_fwd_f32(FwdParams p) {
     clear = refresh_decision<NW>(m_run, row_valid, min(BQ, N - i * BQ), p.scale,
                                  p.refresh_delta, p.stats + tile, s_part, &s_clear);
   }
-  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk);
-  else write_mask_row<NT>(mrow, p.W, p.Tk, s_keep, i * BQ < p.dense_prefix, exempt_cols);
+  if (clear) clear_mask_row<NT>(mrow, p.W, p.Tk, s_old);
+  else write_mask_row<NT>(mrow, p.W, p.Tk, s_old, s_keep, i * BQ < p.dense_prefix, exempt_cols);
 }
 
 // ---------------------------------------------------------------------------------------

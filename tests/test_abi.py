@@ -203,3 +203,14 @@ def test_static_workspace_entry_point_rejects_large_problems_without_a_device_ca
     empty = tsa.lite_attn_create(1, 0, 100, 64, tile_q=64)
     assert lib.lite_attn_step_scheduled_static(empty.ptr, None, None, None, None, None,
                                                ctypes.c_float(-1.0), 0, None) == binding.OK
+
+
+def test_create_rejects_heads_spanning_2_gib_in_bf16():
+    """The bf16 kernels address a head's rows through a 32-bit buffer offset."""
+    n, d = 131072, 128
+    ok = tsa.make_config(1, 1, n, d, strides=(0, 0, 8192))       # 2 GiB - 16 KiB + 256 B
+    assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=ok)) == binding.OK
+    big = tsa.make_config(1, 1, n, d, strides=(0, 0, 8200))
+    assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=big)) == binding.ERR_UNSUPPORTED
+    f32 = tsa.make_config(1, 1, n, d, strides=(0, 0, 8200), dtype="fp32")
+    assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=f32)) == binding.OK
