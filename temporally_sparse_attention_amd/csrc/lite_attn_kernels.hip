@@ -464,7 +464,10 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
   float l_run = 0.f;         // this lane's partial row sum
   const float c2 = p.scale_log2;
   const float inv_c2 = 1.f / c2;
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // In a register rather than a literal: the row-sum v_dot2 then encodes in 4 bytes instead of 8
+  // (measured +1% on the 75600-token workload, from its sparse steps).
+  bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  asm volatile("" : "+v"(ones));
 
   // Software pipeline. Iteration n of the tile loop overlaps the matrix work of one tile with
   // the vector work of another, so that a wave keeps the MFMA pipe busy while it computes its
