@@ -516,6 +516,15 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
     }
   };
   // O^T += V^T P^T: lane holds query l32 and features 32db + 8(r/4) + 4*half + (r%4).
+  // The same with the first RING operands already read (early V reads, see phase_a_sched_v).
+  auto pv_mfma_pre = [&](const unsigned char* vst, const bf16x8 (&pb)[4], bf16x8 (&vr)[RING]) {
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      const int db = t % (D / 32), kc = t / (D / 32);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[t % RING], pb[kc], o[db], 0, 0, 0);
+      if (t + RING < D / 8) vr[t % RING] = vread(vst, t + RING);
+    }
+  };
   auto pv_mfma = [&](const unsigned char* vst, const bf16x8 (&pb)[4]) {
     bf16x8 vr[RING];
 #pragma unroll
@@ -651,6 +660,29 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
       __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
     }
   };
+  // Early V reads (D = 128): V(n) is resident from the iteration's barrier on, so the first RING
+  // V^T operand reads of phase B take the slots of the last QK MFMAs of phase A, which read no
+  // K operand, and phase B starts with an MFMA instead of waiting for its reads (measured +0.6%
+  // at D = 128, -1% at D = 64).
+  auto phase_a_sched_v = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);    // K operand reads
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);       // VALU / transcendental
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K reads
+      else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                    // then V reads
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+  };
+  auto phase_b_sched_v = [&]() {
+#pragma unroll
+    for (int t = 0; t < D / 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+    }
+  };
   auto phase_b_sched = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * RING, 0);   // V operand reads
 #pragma unroll
@@ -686,19 +718,33 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
     if (!skip) {
       // phase A. After the last tile, K(n+1) is a stale stage: its scores are never used.
       bf16x8 pb[4];
-      qk_mfma(kst, tn);
-      l_run += exp_pack(tc, pb);
-      phase_a_sched();
-      // In-step skip masks the ragged tile between the phases: it has more live registers, and
-      // in the whole-body form below (tile n's exponentials kept in phase A) it spills.
-      if constexpr (INSTEP) {
-        if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
+      if constexpr (!INSTEP && D == 128) {
+        qk_mfma(kst, tn);
+        l_run += exp_pack(tc, pb);
+        bf16x8 vr[RING];
+#pragma unroll
+        for (int t = 0; t < RING; ++t) vr[t] = vread(vst, t);
+        phase_a_sched_v();
+        // phase B
+        nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
+        pv_mfma_pre(vst, pb, vr);
+        mt1 = scale_max(tn, nb, tm);
+        phase_b_sched_v();
+      } else {
+        qk_mfma(kst, tn);
+        l_run += exp_pack(tc, pb);
+        phase_a_sched();
+        // In-step skip masks the ragged tile between the phases: it has more live registers,
+        // and in the whole-body form below (tile n's exponentials kept in phase A) it spills.
+        if constexpr (INSTEP) {
+          if (live && (j1 + 1) * BK > N) mask_ragged(j1, tn);
+        }
+        // phase B
+        nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
+        pv_mfma(vst, pb);
+        mt1 = scale_max(tn, nb, tm);
+        phase_b_sched();
       }
-      // phase B
-      nb = m_ref == -INFINITY ? 0.f : -m_ref * c2;   // exponent reference for tile n+1
-      pv_mfma(vst, pb);
-      mt1 = scale_max(tn, nb, tm);
-      phase_b_sched();
       // The ragged last key tile is fixed up after phase B rather than masked between the two
       // phases: a branch there would split the body into two basic blocks, and the compiler
       // would then move tile n's exponentials out of phase A. The empty asm keeps the maxima
