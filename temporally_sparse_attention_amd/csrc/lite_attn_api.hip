@@ -372,7 +372,8 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     if (!p.queue) p.n_cu = 0;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;
-      const hipError_t e = lite_attn::launch_plan(mask, n, h->W, h->Tk, workspace, st);
+      const hipError_t e =
+          lite_attn::launch_plan(mask, n, h->Tq, h->W, h->Tk, p.descending, workspace, st);
       if (e != hipSuccess)
         return fail(LITE_ATTN_ERR_HIP, "%s: schedule launch failed: %s", who,
                     hipGetErrorString(e));

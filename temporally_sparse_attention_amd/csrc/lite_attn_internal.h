@@ -51,11 +51,12 @@ hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t strea
 // Device address of tile queue `slot` (0 <= slot < kQueueSlots) on the current device.
 hipError_t tile_queue_address(int slot, uint32_t** out);
 
-// Heaviest-first schedule of the query tiles of a mask: the workspace receives the block ->
-// tile permutation (n_tiles uint32 at offset 0) and scratch bucket bytes after it.
+// Schedule of the query tiles of a step from their visit counts (heavy tiles first, then heads by
+// decreasing work, each in traversal direction): the workspace receives the queue position ->
+// tile permutation (n_tiles uint32 at offset 0) and the per-tile counts after it.
 size_t plan_workspace_bytes(int64_t n_tiles);
-hipError_t launch_plan(const uint32_t* mask, int n_tiles, int W, int Tk, void* workspace,
-                       hipStream_t stream);
+hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk, int descending,
+                       void* workspace, hipStream_t stream);
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,
                                 int Tq, int Tk, int W, hipStream_t stream);
 

@@ -1148,16 +1148,20 @@ __global__ void __launch_bounds__(256) mask_fill_zero(uint32_t* mask, size_t wor
     mask[w] = 0u;
 }
 
-// Heaviest-first schedule (LiteAttention, page 1 "Architecture Overview": a skip list for high
-// sparsity; its list lengths are the per-tile work). A first kernel counts, per query tile, the
-// key tiles it will visit. A single workgroup of 1024 threads then orders the tiles: a tile is
-// heavy when it visits at least half of all key tiles and at least four times the mean count (a
-// dense prefix row in a sparse step, say). Heavy tiles go first, then every other tile, each
-// group in natural order: the long workgroups then start first instead of setting the tail,
-// while neighbouring query tiles (which share K/V through the caches) still run together. Each
-// thread takes a contiguous range of tiles, and a scan over (group, thread) gives every tile
-// its position.
+// Schedule of a step from its visit counts (LiteAttention, page 1 "Architecture Overview": a skip
+// list for high sparsity; its list lengths are the per-tile work). A first kernel counts, per
+// query tile, the key tiles it will visit. A single workgroup of 1024 threads then orders the
+// tiles for the persistent launch:
+//  1. heavy tiles first, in natural order: a tile is heavy when it visits at least half of all
+//     key tiles and at least four times the mean count (a dense-prefix row in a sparse step);
+//  2. then the other tiles head by head, heads in decreasing order of their remaining work
+//     (ties by index), and within a head in the direction of the step's key traversal.
+// Long work starts first, so the last tiles handed out belong to the lightest head and the
+// launch ends with a short tail, while neighbouring query tiles of a head (which share K/V
+// through the caches) still run together. With more than kPlanHeads heads the heads keep their
+// natural order.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanHeads = 1024;
 
 // Per query tile: the number of key tiles it will visit (one thread per tile).
 __global__ void __launch_bounds__(256) plan_count(const uint32_t* mask, int n, int W, int Tk,
@@ -1170,15 +1174,39 @@ __global__ void __launch_bounds__(256) plan_count(const uint32_t* mask, int n, i
   count[x] = (uint16_t)c;
 }
 
-__global__ void __launch_bounds__(kPlanThreads) plan_heaviest_first(const uint16_t* count, int n,
-                                                                    int Tk, uint32_t* perm) {
-  __shared__ uint32_t s_cnt[2 * kPlanThreads];   // [group][thread], group 0: heavy
-  __shared__ uint32_t s_part[kPlanThreads];
-  __shared__ unsigned long long s_total;
+// Exclusive scan of v over the 1024 threads of the workgroup (s: kPlanThreads words of LDS).
+__device__ uint32_t plan_exclusive_scan(uint32_t v, uint32_t* s) {
   const int t = threadIdx.x;
+  s[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const uint32_t u = t >= off ? s[t - off] : 0u;
+    __syncthreads();
+    s[t] += u;
+    __syncthreads();
+  }
+  const uint32_t incl = s[t];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_order(const uint16_t* count, int n, int Tq,
+                                                           int Tk, int descending,
+                                                           uint32_t* perm) {
+  __shared__ uint32_t s_scan[kPlanThreads];
+  __shared__ unsigned long long s_work[kPlanHeads];   // remaining work per head
+  __shared__ uint32_t s_pre[kPlanHeads + 1];          // other tiles before each head's first
+  __shared__ uint32_t s_base[kPlanHeads];             // rank -> head, then head -> first position
+  __shared__ unsigned long long s_total;
+  __shared__ uint32_t s_heavy;
+  const int t = threadIdx.x;
+  const int heads = n / Tq;
+  const bool by_work = heads <= kPlanHeads;
+  // every thread walks a contiguous range of tiles (natural order) in each pass
   const int per = (n + kPlanThreads - 1) / kPlanThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
   if (t == 0) s_total = 0ull;
+  for (int h = t; h < kPlanHeads; h += kPlanThreads) s_work[h] = 0ull;
   __syncthreads();
   unsigned long long sum = 0ull;
   for (int x = lo; x < hi; ++x) sum += count[x];
@@ -1189,34 +1217,73 @@ __global__ void __launch_bounds__(kPlanThreads) plan_heaviest_first(const uint16
   auto heavy = [&](int c) {
     return 2 * c >= Tk && (unsigned long long)c * (unsigned long long)n >= 4ull * total;
   };
-  uint32_t nh = 0u, nr = 0u;
-  for (int x = lo; x < hi; ++x) {
-    if (heavy(count[x])) ++nh;
-    else ++nr;
+  // 1. heavy tiles in natural order
+  uint32_t nh = 0u;
+  for (int x = lo; x < hi; ++x) nh += heavy(count[x]) ? 1u : 0u;
+  uint32_t at = plan_exclusive_scan(nh, s_scan);
+  if (t == kPlanThreads - 1) s_heavy = at + nh;
+  for (int x = lo; x < hi; ++x)
+    if (heavy(count[x])) perm[at++] = (uint32_t)x;
+  // 2. the other tiles: their natural-order prefix count, per-head starts and work
+  uint32_t pre = plan_exclusive_scan((uint32_t)(hi - lo) - nh, s_scan);
+  const uint32_t pre_lo = pre;
+  __syncthreads();
+  const uint32_t n_heavy = s_heavy;
+  if (!by_work) {   // natural head order
+    for (int x = lo; x < hi; ++x)
+      if (!heavy(count[x])) perm[n_heavy + pre++] = (uint32_t)x;
+    return;
   }
-  s_cnt[t] = nh;
-  s_cnt[kPlanThreads + t] = nr;
-  __syncthreads();
-  // exclusive scan over the 2 * 1024 counts in [group][thread] order: thread t scans its two
-  // consecutive entries, then the 1024 partial sums are scanned
-  const uint32_t e0 = s_cnt[2 * t], e1 = s_cnt[2 * t + 1];
-  s_part[t] = e0 + e1;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const uint32_t v = t >= off ? s_part[t - off] : 0u;
-    __syncthreads();
-    s_part[t] += v;
-    __syncthreads();
+  {
+    unsigned long long w = 0ull;
+    int h_cur = lo < hi ? lo / Tq : 0;
+    for (int x = lo; x < hi; ++x) {
+      const int h = x / Tq;
+      if (h != h_cur) {
+        atomicAdd(&s_work[h_cur], w);
+        w = 0ull;
+        h_cur = h;
+      }
+      if (x == h * Tq) s_pre[h] = pre;
+      const int c = count[x];
+      if (!heavy(c)) {
+        w += (unsigned long long)c;
+        ++pre;
+      }
+    }
+    if (lo < hi) atomicAdd(&s_work[h_cur], w);
+    if (hi == n && lo < hi) s_pre[heads] = pre;
+    if (n == 0 && t == 0) s_pre[0] = 0u;
   }
-  const uint32_t base = s_part[t] - (e0 + e1);
   __syncthreads();
-  s_cnt[2 * t] = base;
-  s_cnt[2 * t + 1] = base + e0;
+  // rank of each head: heavier first, ties by index
+  for (int h = t; h < heads; h += kPlanThreads) {
+    const unsigned long long w = s_work[h];
+    uint32_t rank = 0u;
+    for (int g = 0; g < heads; ++g) {
+      const unsigned long long wg = s_work[g];
+      rank += (wg > w || (wg == w && g < h)) ? 1u : 0u;
+    }
+    s_base[rank] = (uint32_t)h;   // rank -> head
+  }
   __syncthreads();
-  uint32_t at_heavy = s_cnt[t], at_rest = s_cnt[kPlanThreads + t];
+  uint32_t my_head = 0u, my_rest = 0u;
+  if (t < heads) {
+    my_head = s_base[t];
+    my_rest = s_pre[my_head + 1] - s_pre[my_head];
+  }
+  __syncthreads();
+  const uint32_t before = plan_exclusive_scan(my_rest, s_scan);
+  if (t < heads) s_base[my_head] = n_heavy + before;   // head -> first position
+  __syncthreads();
+  // 3. each head's other tiles in the direction of the step's key traversal
+  pre = pre_lo;
   for (int x = lo; x < hi; ++x) {
-    if (heavy(count[x])) perm[at_heavy++] = (uint32_t)x;
-    else perm[at_rest++] = (uint32_t)x;
+    if (heavy(count[x])) continue;
+    const int h = x / Tq;
+    const uint32_t within = pre++ - s_pre[h];
+    const uint32_t rest = s_pre[h + 1] - s_pre[h];
+    perm[s_base[h] + (descending ? rest - 1u - within : within)] = (uint32_t)x;
   }
 }
 
@@ -1317,8 +1384,8 @@ size_t plan_workspace_bytes(int64_t n_tiles) {
   return ((size_t)n_tiles * 4 + 255) / 256 * 256 + ((size_t)n_tiles * 2 + 255) / 256 * 256;
 }
 
-hipError_t launch_plan(const uint32_t* mask, int n_tiles, int W, int Tk, void* workspace,
-                       hipStream_t stream) {
+hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk, int descending,
+                       void* workspace, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   uint32_t* perm = static_cast<uint32_t*>(workspace);
   uint16_t* count = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
@@ -1329,8 +1396,8 @@ hipError_t launch_plan(const uint32_t* mask, int n_tiles, int W, int Tk, void* w
                                  stream);
   if (e != hipSuccess) return e;
   const uint16_t* ccount = count;
-  void* args[] = {&ccount, &n_tiles, &Tk, &perm};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&plan_heaviest_first), dim3(1),
+  void* args[] = {&ccount, &n_tiles, &Tq, &Tk, &descending, &perm};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&plan_order), dim3(1),
                          dim3(kPlanThreads), args, 0, stream);
 }
 

@@ -1,6 +1,6 @@
-"""Heaviest-first scheduling (lite_attn_step_scheduled): the same results as lite_attn_step, bit
-for bit, and the documented tile order (heavy query tiles first, then the rest, each group in
-natural order)."""
+"""Scheduled steps (lite_attn_step_scheduled): the same results as lite_attn_step, bit for bit,
+and the documented tile order (heavy query tiles first in natural order, then the other tiles
+head by head, heads by decreasing work, each head in the step's traversal direction)."""
 import numpy as np
 import pytest
 import torch
@@ -12,13 +12,25 @@ from workloads import Workload, derive, get_config
 pytestmark = pytest.mark.gpu
 
 
-def expected_order(mask_np: np.ndarray, tiles_k: int) -> np.ndarray:
+def expected_order(mask_np: np.ndarray, tiles_k: int, tiles_q: int, descending: bool) -> np.ndarray:
     """Reference tile order for a mask [B, H, Tq, W]: tiles visiting at least half of all key
-    tiles and at least four times the mean first, then the others, each in natural order."""
+    tiles and at least four times the mean first, in natural order; then, head by head, heads by
+    decreasing work left (sum of their other tiles' visit counts; ties by index), each head's
+    other tiles in the direction of the step's key traversal."""
     bits = mask_to_bits(mask_np, tiles_k).reshape(-1, tiles_k)
     count = (tiles_k - bits.sum(axis=1)).astype(np.int64)
-    heavy = (2 * count >= tiles_k) & (count * count.size >= 4 * count.sum())
-    return np.argsort(~heavy, kind="stable")
+    n = count.size
+    heavy = (2 * count >= tiles_k) & (count * n >= 4 * count.sum())
+    order = list(np.nonzero(heavy)[0])
+    heads = n // tiles_q
+    if heads > 1024:
+        return np.array(order + list(np.nonzero(~heavy)[0]))
+    work = [int(count[h * tiles_q:(h + 1) * tiles_q][~heavy[h * tiles_q:(h + 1) * tiles_q]].sum())
+            for h in range(heads)]
+    for h in sorted(range(heads), key=lambda h: (-work[h], h)):
+        rows = range(tiles_q - 1, -1, -1) if descending else range(tiles_q)
+        order += [h * tiles_q + i for i in rows if not heavy[h * tiles_q + i]]
+    return np.array(order)
 
 
 CASES = [
@@ -48,7 +60,8 @@ def test_scheduled_step_matches_plain_step(label, cid, kw, steps):
         assert torch.equal(o_plain, o_sched), f"{label} step {t}: outputs differ"
         assert torch.equal(m_plain, m_sched), f"{label} step {t}: masks differ"
         perm = ws[:4 * n].view(torch.int32).cpu().numpy()
-        assert np.array_equal(perm, expected_order(start, tk)), f"{label} step {t}: order"
+        desc = cfg.order == "alt" and t % 2 == 1
+        assert np.array_equal(perm, expected_order(start, tk, tq, desc)), f"{label} step {t}: order"
         log(f"  [{label}] step {t}: first tiles {perm[:6].tolist()}")
 
 
@@ -76,7 +89,7 @@ def test_scheduled_full_size_order_and_result():
     assert torch.equal(o1, o2) and torch.equal(m1, m2)
     n = cfg.batch * cfg.heads * tq
     perm = ws[:4 * n].view(torch.int32).cpu().numpy()
-    assert np.array_equal(perm, expected_order(start, tk))
+    assert np.array_equal(perm, expected_order(start, tk, tq, False))
     # the prefix query tiles (rows [0, 256) of every head) are never skipped, so in a sparse
     # step they are heavy and run first
     bits = mask_to_bits(start, tk).reshape(-1, tk)
