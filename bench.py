@@ -66,7 +66,7 @@ def parse_args():
                     help="use lite_attn_step_refresh with this divergence budget (mask rows whose "
                          "statistic moves by more are cleared)")
     ap.add_argument("--calibrate", default=None, metavar="LO,HI",
-                    help="derive the log_eps schedule with calibrate_schedule (untimed, before the "
+                    help="derive the log_eps schedule with lite_attn_calibrate (untimed, before the "
                          "warmup) from output-error budgets rising linearly from LO to HI (max "
                          "|out - dense|), and time that schedule instead of the workload's")
     ap.add_argument("--in-step-skip", action="store_true",
@@ -322,8 +322,7 @@ def main():
         n_st = cfg.steps
         budgets = [lo + (hi - lo) * t / max(1, n_st - 1) for t in range(n_st)]
         log(f"[bench] calibrating log_eps for budgets {lo} .. {hi}")
-        res = tsa.calibrate_schedule(tsa.LiteAttentionRunner(att, dev),
-                                     lambda t: (qs[t], ks[t], v), n_st, budgets)
+        res = att.calibrate(qs[:n_st], ks[:n_st], [v] * n_st, budgets)
         log_eps = list(res.log_eps)
         calibration = res.as_dict()
         calibration["log_eps"] = [None if math.isinf(x) else x for x in res.log_eps]

@@ -233,6 +233,53 @@ int lite_attn_reset_mask(lite_attn_t handle, uint32_t* mask, void* stream);
 int lite_attn_mask_popcount(lite_attn_t handle, const uint32_t* mask, uint32_t* counts,
                             void* stream);
 
+/* Largest absolute difference between two outputs of this handle: *result (a device float
+ * written on `stream`) = max over every valid element (b, h, n, d < head_dim) of |a - b|, each
+ * difference taken in float32 after widening bf16 exactly; NaN when any difference is NaN, 0
+ * when B*H*N == 0. a and b are read through the handle's strides and dtype, like out; the
+ * memory between rows is not read. This is the output error that the per-step budgets of
+ * lite_attn_calibrate bound. LiteAttention, page 1 "Architecture Overview" (accumulated-error
+ * calibration). Pointers 16-byte aligned (result: 4-byte). Returns INVALID_ARG for NULL or
+ * misaligned pointers, HIP when a launch fails. */
+int lite_attn_output_max_abs_diff(lite_attn_t handle, const void* a, const void* b,
+                                  float* result, void* stream);
+
+/* Bytes of device workspace that lite_attn_calibrate needs: four outputs under the handle's
+ * strides, two masks and one result word, each part rounded up to 256 bytes (0 for a NULL
+ * handle). */
+size_t lite_attn_calibrate_workspace_bytes(lite_attn_t handle);
+
+/* Choose the per-step error budgets log_eps_t from per-step output-error limits.
+ * LiteAttention, page 1 "Architecture Overview": each denoising step gets its own error budget
+ * from accumulated-error calibration, early steps tolerating less error.
+ *
+ * The flags of step t first change the output of step t+1. So, for t < steps - 1, log_eps[t]
+ * receives the loosest of `candidates` (largest first) whose flags, OR-ed into the mask carried
+ * from steps 0..t-1, keep the error of step t+1's output against dense attention within
+ * error_budgets[t + 1]; -inf (flag nothing) when none does. The last step's flags change no
+ * output: it keeps the previous step's choice (-inf when steps == 1). The error is
+ * lite_attn_output_max_abs_diff of the step's output against that of the same step with an
+ * empty mask, and errors[t] receives the error of step t under the chosen schedule (step 0's is
+ * 0: its mask is empty). The mask starts empty and accumulates every flag since step 0, as in a
+ * generation. Each step runs as lite_attn_step with this handle (its order, dense prefix and
+ * options), step index t.
+ *
+ * q, k, v: host arrays of `steps` device pointers, step t's inputs (each as for
+ * lite_attn_step). error_budgets: host array of `steps` limits (not NaN; error_budgets[0] is
+ * not used). candidates: host array of n_candidates values in [-inf, 0] (duplicates are
+ * dropped; may be NULL when n_candidates == 0, and then every step gets -inf). log_eps, errors:
+ * host arrays of `steps` floats, written. workspace: lite_attn_calibrate_workspace_bytes(handle)
+ * bytes of device memory, 256-byte aligned, overwritten (it may be NULL when B*H*N == 0).
+ * The call runs on `stream` and waits for it after every error it measures, so it blocks the
+ * host and the stream must not be capturing (INVALID_ARG). It runs about
+ * steps * (2 + 2 * tried candidates) attention steps. Returns INVALID_ARG for NULL or misaligned
+ * arguments, negative steps or n_candidates, a NaN budget, a NaN or positive candidate;
+ * otherwise what the steps and reductions return. */
+int lite_attn_calibrate(lite_attn_t handle, const void* const* q, const void* const* k,
+                        const void* const* v, int32_t steps, const float* error_budgets,
+                        const float* candidates, int32_t n_candidates, float* log_eps,
+                        float* errors, void* workspace, void* stream);
+
 /* Static English name of a status code. */
 const char* lite_attn_status_string(int status);
 

@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     Handle,
     LiteAttnError,
+    lite_attn_calibrate,
+    lite_attn_calibrate_workspace_bytes,
     lite_attn_create,
     lite_attn_destroy,
     lite_attn_last_error,
@@ -22,6 +24,7 @@ from .binding import (  # noqa: F401
     lite_attn_mask_bytes,
     lite_attn_mask_geometry,
     lite_attn_mask_popcount,
+    lite_attn_output_max_abs_diff,
     lite_attn_reset_mask,
     lite_attn_status_string,
     lite_attn_step,
@@ -32,6 +35,7 @@ from .binding import (  # noqa: F401
     make_config,
 )
 from .schedule import (  # noqa: F401
+    DEFAULT_CANDIDATES,
     CalibrationResult,
     ErrorBudgetSchedule,
     LiteAttentionRunner,
@@ -114,3 +118,26 @@ class LiteAttention:
         if total == 0:
             return 0.0
         return float(self.popcount(mask).to("cpu").long().sum().item()) / total
+
+    def max_abs_diff(self, a, b, result=None, stream=None):
+        """Device float32 [1] tensor holding max |a - b| over the valid elements; asynchronous."""
+        import torch
+        if result is None:
+            result = torch.empty(1, dtype=torch.float32, device=a.device)
+        lite_attn_output_max_abs_diff(self.handle, a, b, result, stream)
+        return result
+
+    def new_calibration_workspace(self, device):
+        import torch
+        return torch.empty(max(1, lite_attn_calibrate_workspace_bytes(self.handle)),
+                           dtype=torch.uint8, device=device)
+
+    def calibrate(self, qs, ks, vs, error_budgets, candidates=DEFAULT_CANDIDATES,
+                  workspace=None, stream=None) -> CalibrationResult:
+        """Per-step budgets log_eps_t from per-step output-error limits, chosen by the library
+        (lite_attn_calibrate); qs, ks, vs hold one device tensor per step. Blocks until done."""
+        if workspace is None and len(qs):
+            workspace = self.new_calibration_workspace(qs[0].device)
+        log_eps, errors = lite_attn_calibrate(self.handle, qs, ks, vs, error_budgets, candidates,
+                                              workspace, stream)
+        return CalibrationResult(log_eps, errors, [float(x) for x in error_budgets])

@@ -33,6 +33,9 @@ EXPORTS = (
     "lite_attn_step_scheduled_static",
     "lite_attn_reset_mask",
     "lite_attn_mask_popcount",
+    "lite_attn_output_max_abs_diff",
+    "lite_attn_calibrate_workspace_bytes",
+    "lite_attn_calibrate",
     "lite_attn_status_string",
     "lite_attn_last_error",
     "lite_attn_last_launch",
@@ -121,6 +124,15 @@ def _load() -> ctypes.CDLL:
     lib.lite_attn_reset_mask.restype = ctypes.c_int
     lib.lite_attn_mask_popcount.argtypes = [vp, vp, vp, vp]
     lib.lite_attn_mask_popcount.restype = ctypes.c_int
+    lib.lite_attn_output_max_abs_diff.argtypes = [vp, vp, vp, vp, vp]
+    lib.lite_attn_output_max_abs_diff.restype = ctypes.c_int
+    lib.lite_attn_calibrate_workspace_bytes.argtypes = [vp]
+    lib.lite_attn_calibrate_workspace_bytes.restype = ctypes.c_size_t
+    f32p = ctypes.POINTER(ctypes.c_float)
+    vpp = ctypes.POINTER(vp)
+    lib.lite_attn_calibrate.argtypes = [vp, vpp, vpp, vpp, ctypes.c_int32, f32p, f32p,
+                                        ctypes.c_int32, f32p, f32p, vp, vp]
+    lib.lite_attn_calibrate.restype = ctypes.c_int
     lib.lite_attn_status_string.argtypes = [ctypes.c_int]
     lib.lite_attn_status_string.restype = ctypes.c_char_p
     lib.lite_attn_last_error.argtypes = []
@@ -386,3 +398,57 @@ def lite_attn_mask_popcount(handle: Handle, mask, counts, stream=None):
                                         _ptr(counts, "counts", dev),
                                         ctypes.c_void_p(_stream_ptr(stream, dev))),
            "lite_attn_mask_popcount")
+
+
+def lite_attn_output_max_abs_diff(handle: Handle, a, b, result, stream=None):
+    """Enqueue result[0] = max |a - b| over the valid elements (float32 device tensor)."""
+    for t, name in ((a, "a"), (b, "b")):
+        _check_qkvo(handle, t, name)
+    torch = _torch()
+    if isinstance(result, torch.Tensor) and (result.dtype != torch.float32 or
+                                             result.numel() < 1):
+        raise ValueError("result must be a float32 tensor with at least one element")
+    dev = None if isinstance(a, int) else a.device
+    _check(_lib.lite_attn_output_max_abs_diff(handle.ptr, _ptr(a, "a", dev), _ptr(b, "b", dev),
+                                              _ptr(result, "result", dev),
+                                              ctypes.c_void_p(_stream_ptr(stream, dev))),
+           "lite_attn_output_max_abs_diff")
+
+
+def lite_attn_calibrate_workspace_bytes(handle: Handle) -> int:
+    return int(_lib.lite_attn_calibrate_workspace_bytes(handle.ptr))
+
+
+def lite_attn_calibrate(handle: Handle, qs, ks, vs, error_budgets, candidates, workspace,
+                        stream=None):
+    """Per-step budgets from per-step output-error limits; blocks until done. qs, ks, vs: one
+    device tensor (or pointer) per step. Returns (log_eps, errors) as lists of floats."""
+    steps = len(error_budgets)
+    if not (len(qs) == len(ks) == len(vs) == steps):
+        raise ValueError("one q, k, v and error budget per step is needed")
+    for seq, name in ((qs, "q"), (ks, "k"), (vs, "v")):
+        for t in seq:
+            _check_qkvo(handle, t, name)
+    torch = _torch()
+    need = lite_attn_calibrate_workspace_bytes(handle)
+    if isinstance(workspace, torch.Tensor):
+        if (not workspace.is_contiguous() or
+                workspace.numel() * workspace.element_size() < need):
+            raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes")
+    first = qs[0] if steps else None
+    dev = None if (first is None or isinstance(first, int)) else first.device
+    arr = ctypes.c_void_p * max(1, steps)
+    qa = arr(*[_ptr(t, "q", dev) for t in qs])
+    ka = arr(*[_ptr(t, "k", dev) for t in ks])
+    va = arr(*[_ptr(t, "v", dev) for t in vs])
+    fl = ctypes.c_float * max(1, steps)
+    budgets = fl(*[float(x) for x in error_budgets])
+    cands = (ctypes.c_float * max(1, len(candidates)))(*[float(x) for x in candidates])
+    log_eps, errors = fl(), fl()
+    ws = 0 if workspace is None else _ptr(workspace, "workspace", dev)
+    _check(_lib.lite_attn_calibrate(handle.ptr, qa, ka, va, ctypes.c_int32(steps), budgets,
+                                    cands, ctypes.c_int32(len(candidates)), log_eps, errors,
+                                    ctypes.c_void_p(ws),
+                                    ctypes.c_void_p(_stream_ptr(stream, dev) if steps else 0)),
+           "lite_attn_calibrate")
+    return [float(log_eps[t]) for t in range(steps)], [float(errors[t]) for t in range(steps)]

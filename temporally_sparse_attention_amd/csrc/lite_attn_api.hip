@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -14,6 +15,7 @@
 #include <new>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "lite_attn.h"
 #include "lite_attn_internal.h"
@@ -391,6 +393,28 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
   }
 }
 
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Bytes spanned by one output tensor under the handle's strides, rounded up to 256.
+size_t output_span_bytes(lite_attn_t h) {
+  const lite_attn_config& c = h->cfg;
+  if ((int64_t)c.batch * c.heads * c.seq_len == 0) return 0;
+  const int64_t elems = (int64_t)(c.batch - 1) * h->sb + (int64_t)(c.heads - 1) * h->sh +
+                        (int64_t)(c.seq_len - 1) * h->sn + c.head_dim;
+  return round256((size_t)elems * (c.dtype == LITE_ATTN_BF16 ? 2 : 4));
+}
+
+int max_abs_diff_impl(const char* who, lite_attn_t h, const void* a, const void* b,
+                      float* result, hipStream_t st) {
+  const lite_attn_config& c = h->cfg;
+  const hipError_t e = lite_attn::launch_output_max_abs_diff(
+      a, b, c.dtype == LITE_ATTN_BF16, c.batch, c.heads, c.seq_len, c.head_dim, h->sb, h->sh,
+      h->sn, result, st);
+  return e == hipSuccess ? LITE_ATTN_OK
+                         : fail(LITE_ATTN_ERR_HIP, "%s: reduction launch failed: %s", who,
+                                hipGetErrorString(e));
+}
+
 }  // namespace
 
 extern "C" {
@@ -488,6 +512,142 @@ int lite_attn_mask_popcount(lite_attn_t h, const uint32_t* mask, uint32_t* count
   if (e != hipSuccess)
     return fail(LITE_ATTN_ERR_HIP, "mask_popcount: launch failed: %s", hipGetErrorString(e));
   return LITE_ATTN_OK;
+}
+
+int lite_attn_output_max_abs_diff(lite_attn_t h, const void* a, const void* b, float* result,
+                                  void* stream) {
+  static const char* who = "output_max_abs_diff";
+  if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL handle", who);
+  if (!result || !aligned(result, 4))
+    return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or misaligned result", who);
+  const lite_attn_config& c = h->cfg;
+  if ((int64_t)c.batch * c.heads * c.seq_len > 0 &&
+      (!a || !b || !aligned(a, 16) || !aligned(b, 16)))
+    return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or misaligned tensor (16 B needed)", who);
+  return max_abs_diff_impl(who, h, a, b, result, static_cast<hipStream_t>(stream));
+}
+
+size_t lite_attn_calibrate_workspace_bytes(lite_attn_t h) {
+  if (!h) return 0;
+  return 4 * output_span_bytes(h) + 2 * round256(lite_attn_mask_bytes(h)) + 256;
+}
+
+int lite_attn_calibrate(lite_attn_t h, const void* const* q, const void* const* k,
+                        const void* const* v, int32_t steps, const float* error_budgets,
+                        const float* candidates, int32_t n_candidates, float* log_eps,
+                        float* errors, void* workspace, void* stream) {
+  static const char* who = "calibrate";
+  try {
+    if (!h) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL handle", who);
+    if (steps < 0) return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: negative steps %d", who, steps);
+    if (steps == 0) return LITE_ATTN_OK;
+    if (!q || !k || !v || !error_budgets || !log_eps || !errors)
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL host array", who);
+    if (n_candidates < 0 || (n_candidates > 0 && !candidates))
+      return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: bad candidate list", who);
+    for (int t = 0; t < steps; ++t)
+      if (std::isnan(error_budgets[t]))
+        return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: error budget %d is NaN", who, t);
+    std::vector<float> cands(candidates, candidates + n_candidates);
+    for (float x : cands)
+      if (std::isnan(x) || x > 0.f)
+        return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: candidate %g is not in [-inf, 0]", who,
+                    (double)x);
+    std::sort(cands.begin(), cands.end(), [](float a, float b) { return a > b; });
+    cands.erase(std::unique(cands.begin(), cands.end()), cands.end());  // loosest first
+
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const lite_attn_config& c = h->cfg;
+    const bool empty = (int64_t)c.batch * c.heads * c.seq_len == 0;  // no device call at all
+    if (!empty) {
+      if (!workspace || !aligned(workspace, 256))
+        return fail(LITE_ATTN_ERR_INVALID_ARG, "%s: NULL or not 256-byte aligned workspace",
+                    who);
+      hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(st, &capture) != hipSuccess)
+        return fail(LITE_ATTN_ERR_HIP, "%s: cannot query the stream's capture status", who);
+      if (capture != hipStreamCaptureStatusNone)
+        return fail(LITE_ATTN_ERR_INVALID_ARG,
+                    "%s: the stream is capturing; calibration reads its errors back and cannot "
+                    "be recorded into a graph", who);
+    }
+
+    const size_t ob = output_span_bytes(h);
+    const size_t mask_bytes = lite_attn_mask_bytes(h);
+    const size_t mb = round256(mask_bytes);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    void* out_try = w;                 // output of a trial step (discarded)
+    void* out_next = w + ob;           // next step's output under a trial mask
+    void* dense_cur = w + 2 * ob;      // dense output of the current step
+    void* dense_next = w + 3 * ob;     // dense output of the next step
+    uint32_t* mask = empty ? nullptr : reinterpret_cast<uint32_t*>(w + 4 * ob);
+    uint32_t* m_try = empty ? nullptr : reinterpret_cast<uint32_t*>(w + 4 * ob + mb);
+    float* res = empty ? nullptr : reinterpret_cast<float*>(w + 4 * ob + 2 * mb);
+    const size_t words = mask_bytes / sizeof(uint32_t);
+
+    auto run = [&](int t, uint32_t* m, float eps, void* out) {
+      return step_impl(who, h, q[t], k[t], v[t], out, m, eps, t, nullptr, false, nullptr, 0.f,
+                       false, stream);
+    };
+    auto hip_ok = [&](hipError_t e, const char* what) {
+      return e == hipSuccess ? LITE_ATTN_OK
+                             : fail(LITE_ATTN_ERR_HIP, "%s: %s: %s", who, what,
+                                    hipGetErrorString(e));
+    };
+    // dense attention of step t (nothing skipped) into out
+    auto dense = [&](int t, void* out) {
+      int r = hip_ok(lite_attn::launch_mask_fill_zero(m_try, words, st), "mask clear");
+      return r != LITE_ATTN_OK ? r : run(t, m_try, -INFINITY, out);
+    };
+    auto error = [&](const void* a, const void* b, float* err) {
+      *err = 0.f;
+      if (empty) return (int)LITE_ATTN_OK;
+      int r = max_abs_diff_impl(who, h, a, b, res, st);
+      if (r != LITE_ATTN_OK) return r;
+      r = hip_ok(hipMemcpyAsync(err, res, sizeof(float), hipMemcpyDeviceToHost, st), "read-back");
+      return r != LITE_ATTN_OK ? r : hip_ok(hipStreamSynchronize(st), "synchronize");
+    };
+#define CALIB_TRY(x)                     \
+  do {                                   \
+    const int r_ = (x);                  \
+    if (r_ != LITE_ATTN_OK) return r_;   \
+  } while (0)
+
+    // the generation starts with nothing skipped
+    CALIB_TRY(hip_ok(lite_attn::launch_mask_fill_zero(mask, words, st), "mask clear"));
+    CALIB_TRY(dense(0, dense_cur));
+    for (int t = 0; t < steps; ++t) {
+      float pick = -INFINITY;
+      if (t + 1 < steps) {
+        // step t's flags first change step t+1's output: take the loosest candidate whose flags,
+        // added to the mask so far, keep step t+1 within its budget
+        CALIB_TRY(dense(t + 1, dense_next));
+        for (float eps : cands) {
+          if (words)
+            CALIB_TRY(hip_ok(hipMemcpyAsync(m_try, mask, mask_bytes, hipMemcpyDeviceToDevice, st),
+                             "mask copy"));
+          CALIB_TRY(run(t, m_try, eps, out_try));
+          CALIB_TRY(run(t + 1, m_try, -INFINITY, out_next));
+          float err = 0.f;
+          CALIB_TRY(error(out_next, dense_next, &err));
+          if (err <= error_budgets[t + 1]) {
+            pick = eps;
+            break;
+          }
+        }
+      } else if (t > 0) {
+        pick = log_eps[t - 1];  // the last step's flags change no output
+      }
+      CALIB_TRY(run(t, mask, pick, out_try));
+      CALIB_TRY(error(out_try, dense_cur, &errors[t]));
+      log_eps[t] = pick;
+      std::swap(dense_cur, dense_next);
+    }
+#undef CALIB_TRY
+    return LITE_ATTN_OK;
+  } catch (...) {
+    return fail(LITE_ATTN_ERR_NO_MEMORY, "%s: out of host memory", who);
+  }
 }
 
 }  // extern "C"

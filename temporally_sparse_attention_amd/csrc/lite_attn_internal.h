@@ -60,4 +60,11 @@ hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk,
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,
                                 int Tq, int Tk, int W, hipStream_t stream);
 
+// *result = max |a - b| over the valid elements of two [B][H][N][D] tensors with element strides
+// (sb, sh, sn), in fp32, NaN when any difference is NaN, 0 for an empty shape. Both pointers
+// 16-byte aligned, strides multiples of 8 elements.
+hipError_t launch_output_max_abs_diff(const void* a, const void* b, bool bf16, int B, int H,
+                                      int N, int D, int64_t sb, int64_t sh, int64_t sn,
+                                      float* result, hipStream_t stream);
+
 }  // namespace lite_attn

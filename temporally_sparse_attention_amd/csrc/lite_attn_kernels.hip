@@ -1302,6 +1302,49 @@ __global__ void __launch_bounds__(256) mask_popcount(const uint32_t* mask, uint3
   if (threadIdx.x == 0) counts[blockIdx.x] = s_sum;
 }
 
+// Largest |a - b| over the valid elements of two outputs laid out by the shared strides, the
+// error measure of the per-step budget calibration (LiteAttention, page 1 "Architecture
+// Overview": accumulated-error calibration). Each difference is taken in fp32; |d| is compared
+// as its bit pattern, which orders non-negative floats like their values and puts NaN above
+// +inf, so a NaN anywhere is reported as NaN. *result must hold 0 before the launch.
+template <bool BF16>
+__global__ void __launch_bounds__(256) output_max_abs_diff(const uint4* a, const uint4* b,
+                                                           int64_t chunks, int per_row, int H,
+                                                           int N, int64_t sb, int64_t sh,
+                                                           int64_t sn, uint32_t* result) {
+  constexpr int kElems = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  uint32_t m = 0u;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = c / per_row;
+    const int part = (int)(c - row * per_row);
+    const int n = (int)(row % N);
+    const int64_t bh = row / N;
+    const int64_t off =
+        ((bh / H) * sb + (bh % H) * sh + (int64_t)n * sn + (int64_t)part * kElems) / kElems;
+    const uint4 x = a[off], y = b[off];
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (BF16) {
+        const float d0 = __uint_as_float(xs[w] << 16) - __uint_as_float(ys[w] << 16);
+        const float d1 =
+            __uint_as_float(xs[w] & 0xffff0000u) - __uint_as_float(ys[w] & 0xffff0000u);
+        m = max(m, max(__float_as_uint(fabsf(d0)), __float_as_uint(fabsf(d1))));
+      } else {
+        m = max(m, __float_as_uint(fabsf(__uint_as_float(xs[w]) - __uint_as_float(ys[w]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  __shared__ uint32_t s_max[4];
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(result, max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3])));
+}
+
 // hipLaunchKernel reports the status of this launch only (hipGetLastError would also return
 // errors left behind by other HIP users in the process).
 template <int D, int NW, bool INSTEP>
@@ -1399,6 +1442,25 @@ hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk,
   void* args[] = {&ccount, &n_tiles, &Tq, &Tk, &descending, &perm};
   return hipLaunchKernel(reinterpret_cast<const void*>(&plan_order), dim3(1),
                          dim3(kPlanThreads), args, 0, stream);
+}
+
+hipError_t launch_output_max_abs_diff(const void* a, const void* b, bool bf16, int B, int H,
+                                      int N, int D, int64_t sb, int64_t sh, int64_t sn,
+                                      float* result, hipStream_t stream) {
+  uint32_t* res = reinterpret_cast<uint32_t*>(result);
+  hipError_t e = launch_mask_fill_zero(res, 1, stream);
+  if (e != hipSuccess) return e;
+  int per_row = D / (bf16 ? 8 : 4);
+  int64_t chunks = (int64_t)B * H * N * per_row;
+  if (chunks == 0) return hipSuccess;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const uint4* pa = static_cast<const uint4*>(a);
+  const uint4* pb = static_cast<const uint4*>(b);
+  void* args[] = {&pa, &pb, &chunks, &per_row, &H, &N, &sb, &sh, &sn, &res};
+  const void* fn = bf16 ? reinterpret_cast<const void*>(&output_max_abs_diff<true>)
+                        : reinterpret_cast<const void*>(&output_max_abs_diff<false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total, int Tq,

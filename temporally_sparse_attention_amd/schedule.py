@@ -116,11 +116,14 @@ def calibrate_schedule(runner, inputs, steps: int, error_budgets: Sequence[float
 
 class LiteAttentionRunner:
     """calibrate_schedule runner on the GPU library: x = (q, k, v) device tensors; the error is
-    max |out - ref| over all elements."""
+    max |out - ref| over the valid elements, reduced on the device by the library
+    (lite_attn_output_max_abs_diff). LiteAttention.calibrate runs the same loop inside the
+    library."""
 
     def __init__(self, attention, device):
         self.att = attention
         self.device = device
+        self._result = None
 
     def empty_mask(self):
         return self.att.new_mask(self.device)
@@ -137,4 +140,7 @@ class LiteAttentionRunner:
         return self.step(x, self.empty_mask(), -math.inf, t)[0]
 
     def error(self, out, ref) -> float:
-        return float((out.float() - ref.float()).abs().max().item())
+        import torch
+        if self._result is None:
+            self._result = torch.empty(1, dtype=torch.float32, device=self.device)
+        return float(self.att.max_abs_diff(out, ref, self._result).item())

@@ -214,3 +214,54 @@ def test_create_rejects_heads_spanning_2_gib_in_bf16():
     assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=big)) == binding.ERR_UNSUPPORTED
     f32 = tsa.make_config(1, 1, n, d, strides=(0, 0, 8200), dtype="fp32")
     assert _status(lambda: tsa.lite_attn_create(0, 0, 0, 0, config=f32)) == binding.OK
+
+
+def test_calibration_entries_validate_on_the_host_without_a_device_call():
+    lib = binding.library()
+    h = tsa.lite_attn_create(1, 2, 1000, 128, tile_q=128)
+    p = ctypes.c_void_p(4096)
+    # workspace: four outputs (1 * 2 * 1000 * 128 bf16, contiguous), two masks, one result word
+    out_bytes = (2 * 1000 * 128 * 2 + 255) // 256 * 256
+    mask_bytes = (tsa.lite_attn_mask_bytes(h) + 255) // 256 * 256
+    assert tsa.lite_attn_calibrate_workspace_bytes(h) == 4 * out_bytes + 2 * mask_bytes + 256
+    assert lib.lite_attn_calibrate_workspace_bytes(None) == 0
+    # output_max_abs_diff
+    assert lib.lite_attn_output_max_abs_diff(None, p, p, p, None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_output_max_abs_diff(h.ptr, p, p, None, None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_output_max_abs_diff(h.ptr, p, p, ctypes.c_void_p(4098),
+                                             None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_output_max_abs_diff(h.ptr, None, p, p, None) == binding.ERR_INVALID_ARG
+    assert lib.lite_attn_output_max_abs_diff(h.ptr, ctypes.c_void_p(4104), p, p,
+                                             None) == binding.ERR_INVALID_ARG
+    # calibrate: every argument check comes before the first device call
+    steps = 3
+    ptrs = (ctypes.c_void_p * steps)(*([4096] * steps))
+    fl = ctypes.c_float * steps
+
+    def cal(budgets=(0.1, 0.1, 0.1), cands=(-4.0, -8.0), n=None, handle=h, nsteps=steps,
+            q=ptrs, out=True):
+        c = (ctypes.c_float * max(1, len(cands)))(*cands)
+        le, er = fl(), fl()
+        return lib.lite_attn_calibrate(handle.ptr if handle else None, q, ptrs, ptrs, nsteps,
+                                       fl(*budgets), c, len(cands) if n is None else n,
+                                       le if out else None, er, p, None)
+
+    assert cal(handle=None) == binding.ERR_INVALID_ARG
+    assert cal(nsteps=-1) == binding.ERR_INVALID_ARG
+    assert cal(q=None) == binding.ERR_INVALID_ARG
+    assert cal(out=False) == binding.ERR_INVALID_ARG
+    assert cal(n=-1) == binding.ERR_INVALID_ARG
+    assert cal(budgets=(0.1, math.nan, 0.1)) == binding.ERR_INVALID_ARG
+    assert cal(cands=(-4.0, 0.5)) == binding.ERR_INVALID_ARG
+    assert "candidate" in tsa.lite_attn_last_error()
+    assert cal(cands=(math.nan,)) == binding.ERR_INVALID_ARG
+    assert cal(nsteps=0) == binding.OK                                  # nothing to do
+    # an empty problem needs no workspace and no device: every error is 0, so each step takes
+    # the loosest candidate whose budget 0 meets, and the last step repeats its predecessor
+    e = tsa.lite_attn_create(1, 0, 100, 64, tile_q=64)
+    assert tsa.lite_attn_calibrate_workspace_bytes(e) == 256
+    le, er = fl(), fl()
+    c = (ctypes.c_float * 3)(-8.0, -2.0, -8.0)
+    assert lib.lite_attn_calibrate(e.ptr, ptrs, ptrs, ptrs, steps, fl(1.0, -1.0, 1.0), c, 3, le,
+                                   er, None, None) == binding.OK
+    assert list(le) == [-math.inf, -2.0, -2.0] and list(er) == [0.0] * 3
