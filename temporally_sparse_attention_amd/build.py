@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblite_attn.so"
-SOURCES = ["lite_attn_kernels.hip", "lite_attn_api.hip"]
+SOURCES = ["lite_attn_kernels.hip", "lite_attn_aux.hip", "lite_attn_api.hip"]
 
 
 def hipcc() -> str:

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "lite_attn.h"
+#include "lite_attn_aux.h"
 #include "lite_attn_internal.h"
 
 struct lite_attn_s {
