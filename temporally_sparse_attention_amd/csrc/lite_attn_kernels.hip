@@ -650,6 +650,10 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
   const bool row_exempt = i * BQ < p.dense_prefix;
   const int exempt_cols = (p.dense_prefix + BK - 1) / BK;
 
+  // Vector slots per MFMA group. At D = 64 each MFMA carries about twice the softmax work of one
+  // at D = 128 (8 vector instructions rather than 4); with four slots, phase B's scaling and
+  // maxima trailed the last PV MFMA (measured +1.5% with eight).
+  constexpr int VSLOT = D == 64 ? 8 : 4;
   auto phase_a_sched = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, RING, 0);    // K operand reads
     __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);       // VALU / transcendental
@@ -657,7 +661,7 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
     for (int t = 0; t < D / 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, VSLOT, 0);
     }
   };
   // Early V reads (D = 128): V(n) is resident from the iteration's barrier on, so the first RING
@@ -689,7 +693,7 @@ __device__ __forceinline__ uint32_t bf16_tile_body(uint64_t args, uint32_t w_in,
     for (int t = 0; t < D / 8; ++t) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (t + RING < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+      if (t >= 1) __builtin_amdgcn_sched_group_barrier(0x402, VSLOT, 0);
     }
   };
 
