@@ -8,9 +8,13 @@
  *   - running the same chain twice gives bit-identical outputs and masks;
  *   - the same chain through lite_attn_step_scheduled (heaviest-first order, caller workspace)
  *     and through lite_attn_step_refresh with refresh_delta = +inf (references start as NaN)
- *     gives the plain chain's outputs and masks bit for bit.
+ *     gives the plain chain's outputs and masks bit for bit;
+ *   - lite_attn_output_max_abs_diff of a tensor with itself is 0;
+ *   - lite_attn_calibrate with unlimited error budgets takes the loosest candidate at every step,
+ *     replaying its schedule through lite_attn_step reproduces the errors it reports bit for bit
+ *     (each against the same step with an empty mask), and zero budgets give exact outputs.
  * Exit status 0 means every check passed; the last line printed says "c abi smoke ok".
- * Built by tests/test_c_abi.py with hipcc (host code only) and linked against the library.
+ * Built by tests/test_c_abi.py with gcc as C11 and linked against the library.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -114,6 +118,77 @@ static int run_chain(lite_attn_t h, int mode, const void* dq, const void* dk, co
   CHECK_HIP(hipMemcpy(out_host, dout, sizeof(uint16_t) * (size_t)B * H * N * D,
                       hipMemcpyDeviceToHost));
   CHECK_HIP(hipMemcpy(mask_host, dmask, mask_bytes, hipMemcpyDeviceToHost));
+  return 0;
+}
+
+/* The library's calibration loop (lite_attn_calibrate), checked against a replay of the schedule
+ * it chose. Every step uses the same inputs. */
+static int run_calibration(lite_attn_t h, const void* dq, const void* dk, const void* dv,
+                           void* dout, uint32_t* dmask, size_t mask_bytes) {
+  void *dcal, *ddense;
+  uint32_t* dempty;
+  float* dres;
+  const size_t elems = (size_t)B * H * N * D;
+  const size_t cal_bytes = lite_attn_calibrate_workspace_bytes(h);
+  CHECK_HIP(hipMalloc(&dcal, cal_bytes));
+  CHECK_HIP(hipMalloc(&ddense, elems * 2));
+  CHECK_HIP(hipMalloc((void**)&dempty, mask_bytes));
+  CHECK_HIP(hipMalloc((void**)&dres, sizeof(float)));
+  float r = -1.0f;
+  CHECK_LA(lite_attn_output_max_abs_diff(h, dout, dout, dres, NULL));
+  CHECK_HIP(hipMemcpy(&r, dres, sizeof r, hipMemcpyDeviceToHost));
+  if (r != 0.0f) {
+    fprintf(stderr, "max |a - a| = %g\n", r);
+    return 12;
+  }
+  const void *qs[STEPS], *ks[STEPS], *vs[STEPS];
+  float unlimited[STEPS], zero[STEPS], log_eps[STEPS], errs[STEPS];
+  for (int t = 0; t < STEPS; ++t) {
+    qs[t] = dq;
+    ks[t] = dk;
+    vs[t] = dv;
+    unlimited[t] = INFINITY;
+    zero[t] = 0.0f;
+  }
+  const float cands[3] = {-8.0f, -2.0f, -2.5f};
+  CHECK_LA(lite_attn_calibrate(h, qs, ks, vs, STEPS, unlimited, cands, 3, log_eps, errs, dcal,
+                               NULL));
+  for (int t = 0; t < STEPS; ++t) {
+    printf("calibration step %d: log_eps %g error %g\n", t, log_eps[t], errs[t]);
+    if (log_eps[t] != -2.0f) {
+      fprintf(stderr, "unlimited budgets: step %d took %g, not the loosest candidate\n", t,
+              log_eps[t]);
+      return 13;
+    }
+  }
+  if (errs[0] != 0.0f) {
+    fprintf(stderr, "step 0 starts from an empty mask but reports error %g\n", errs[0]);
+    return 13;
+  }
+  /* replay: the accumulated mask against an empty one, step by step */
+  CHECK_LA(lite_attn_reset_mask(h, dmask, NULL));
+  for (int t = 0; t < STEPS; ++t) {
+    CHECK_LA(lite_attn_step(h, dq, dk, dv, dout, dmask, log_eps[t], t, NULL));
+    CHECK_LA(lite_attn_reset_mask(h, dempty, NULL));
+    CHECK_LA(lite_attn_step(h, dq, dk, dv, ddense, dempty, -INFINITY, t, NULL));
+    CHECK_LA(lite_attn_output_max_abs_diff(h, dout, ddense, dres, NULL));
+    CHECK_HIP(hipMemcpy(&r, dres, sizeof r, hipMemcpyDeviceToHost));
+    if (memcmp(&r, &errs[t], sizeof r) != 0) {
+      fprintf(stderr, "step %d: replayed error %g, calibration reported %g\n", t, r, errs[t]);
+      return 14;
+    }
+  }
+  CHECK_LA(lite_attn_calibrate(h, qs, ks, vs, STEPS, zero, cands, 3, log_eps, errs, dcal, NULL));
+  for (int t = 0; t < STEPS; ++t)
+    if (errs[t] != 0.0f) {
+      fprintf(stderr, "zero budgets: step %d (log_eps %g) has error %g\n", t, log_eps[t],
+              errs[t]);
+      return 15;
+    }
+  CHECK_HIP(hipFree(dcal));
+  CHECK_HIP(hipFree(ddense));
+  CHECK_HIP(hipFree(dempty));
+  CHECK_HIP(hipFree(dres));
   return 0;
 }
 
@@ -235,6 +310,9 @@ int main(void) {
       }
     }
   }
+
+  rc = run_calibration(h, dq, dk, dv, dout, dmask, mask_bytes);
+  if (rc) return rc;
 
   CHECK_HIP(hipFree(dq));
   CHECK_HIP(hipFree(dk));

@@ -3,7 +3,8 @@ include/lite_attn.h and linked against liblite_attn.so (no Python, torch or HIP 
 between). On the CPU it must compile and link; on the GPU it must run a short chain and pass its
 own checks (finite outputs inside the range of V, a non-decreasing skip count, bit-identical
 reruns, argument errors reported, and the scheduled and refresh entry points reproducing the
-plain chain bit for bit)."""
+plain chain bit for bit, and the calibration entries agreeing with a replay of the schedule
+they choose)."""
 import os
 import shutil
 import subprocess
