@@ -192,11 +192,13 @@ size_t lite_attn_workspace_bytes(lite_attn_t handle);
  * aligned, that the call overwrites (it holds nothing between calls). A first kernel reads the
  * mask and counts, per query tile, the key tiles it will visit (its skip-list length). Query
  * tiles that visit at least half of all key tiles and at least four times the mean (dense
- * prefix rows in a sparse step, for example) are scheduled first; the other tiles follow head
- * by head, heads in decreasing order of their remaining work (with more than 1024 heads, in
- * natural order), each head's tiles in the direction of the step's key traversal, which keeps
- * neighbouring query tiles together. The attention kernel then runs its workgroups in that
- * order, so that long work does not start last and set the step's tail. LiteAttention, page 1 "Architecture Overview": the skip list used at high sparsity;
+ * prefix rows in a sparse step, for example) are scheduled first. The shortest tiles go last,
+ * in the step's traversal order: the non-heavy tiles whose list is shorter than a cut, the
+ * largest cut that leaves at most min(16 * compute units, non-heavy tiles / 4) of them. The
+ * other tiles run in between, head by head, heads in decreasing order of their work (with more
+ * than 1024 heads, in natural order), each head's tiles in the direction of the step's key
+ * traversal, which keeps neighbouring query tiles together. The attention kernel then runs its
+ * workgroups in that order, so that long work starts early and the step ends on short tiles. LiteAttention, page 1 "Architecture Overview": the skip list used at high sparsity;
  * here its list lengths drive the schedule. Calls that share a workspace must be ordered on
  * one stream. Returns what lite_attn_step returns, and INVALID_ARG for a NULL or misaligned
  * workspace. */

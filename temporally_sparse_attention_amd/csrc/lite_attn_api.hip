@@ -119,6 +119,23 @@ uint32_t* launch_queue(hipStream_t st, int* n_cu, int* slot_out) {
   return b->second + 2 * slot;
 }
 
+// Compute units of the current device (cached), for a launch that took no tile queue; 0 when the
+// device cannot be queried.
+int device_cus() {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return 0;
+  QueueTable& t = queue_table();
+  std::lock_guard<std::mutex> lock(t.mu);
+  auto c = t.cus.find(cur);
+  if (c == t.cus.end()) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, cur) != hipSuccess)
+      return 0;
+    c = t.cus.emplace(cur, n).first;
+  }
+  return c->second;
+}
+
 // The most recent attention launch of the calling thread (lite_attn_last_launch).
 thread_local int32_t g_last_grid = 0;
 thread_local int32_t g_last_queue = -1;
@@ -375,8 +392,10 @@ int step_impl(const char* who, lite_attn_t h, const void* q, const void* k, cons
     if (!p.queue) p.n_cu = 0;
     if (scheduled) {
       const int n = c.batch * c.heads * h->Tq;
-      const hipError_t e =
-          lite_attn::launch_plan(mask, n, h->Tq, h->W, h->Tk, p.descending, workspace, st);
+      // short tiles at the end of the queue: about eight per workgroup slot (two per CU)
+      const int tail_max = 16 * (p.n_cu > 0 ? p.n_cu : device_cus());
+      const hipError_t e = lite_attn::launch_plan(mask, n, h->Tq, h->W, h->Tk, p.descending,
+                                                  tail_max, workspace, st);
       if (e != hipSuccess)
         return fail(LITE_ATTN_ERR_HIP, "%s: schedule launch failed: %s", who,
                     hipGetErrorString(e));

@@ -10,11 +10,12 @@ namespace lite_attn {
 hipError_t launch_mask_fill_zero(uint32_t* mask, size_t words, hipStream_t stream);
 
 // Schedule of the query tiles of a step from their visit counts (heavy tiles first, then heads by
-// decreasing work, each in traversal direction): the workspace receives the queue position ->
-// tile permutation (n_tiles uint32 at offset 0) and the per-tile counts after it.
+// decreasing work, each in traversal direction, then at most min(tail_max, non-heavy / 4) short
+// tiles in traversal order): the workspace receives the queue position -> tile permutation
+// (n_tiles uint32 at offset 0) and the per-tile counts after it.
 size_t plan_workspace_bytes(int64_t n_tiles);
 hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk, int descending,
-                       void* workspace, hipStream_t stream);
+                       int tail_max, void* workspace, hipStream_t stream);
 // counts[x] = set valid bits of the Tq * W mask words of head x (x < heads_total).
 hipError_t launch_mask_popcount(const uint32_t* mask, uint32_t* counts, int heads_total,
                                 int Tq, int Tk, int W, hipStream_t stream);

@@ -32,17 +32,19 @@ __global__ void __launch_bounds__(256) mask_fill_zero(uint32_t* mask, size_t wor
 // Schedule of a step from its visit counts (LiteAttention, page 1 "Architecture Overview": a skip
 // list for high sparsity; its list lengths are the per-tile work). A first kernel counts, per
 // query tile, the key tiles it will visit. A single workgroup of 1024 threads then orders the
-// tiles for the persistent launch:
+// tiles for the persistent launch in three parts:
 //  1. heavy tiles first, in natural order: a tile is heavy when it visits at least half of all
 //     key tiles and at least four times the mean count (a dense-prefix row in a sparse step);
-//  2. then the other tiles head by head, heads in decreasing order of their remaining work
-//     (ties by index), and within a head in the direction of the step's key traversal.
-// Long work starts first, so the last tiles handed out belong to the lightest head and the
-// launch ends with a short tail, while neighbouring query tiles of a head (which share K/V
-// through the caches) still run together. With more than kPlanHeads heads the heads keep their
-// natural order.
+//  2. then the middle tiles head by head, heads in decreasing order of their middle work (ties by
+//     index), and within a head in the direction of the step's key traversal;
+//  3. last, the short tiles, in the step's traversal order: the non-heavy tiles whose count is
+//     below a cut, the largest cut that leaves at most min(tail_max, non-heavy / 4) of them.
+// Long work starts first, and the launch ends on short tiles, so the workgroups finish close
+// together; neighbouring query tiles of a head (which share K/V through the caches) still run
+// together in parts 2 and 3. With more than kPlanHeads heads the middle keeps the natural order.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanHeads = 1024;
+constexpr int kPlanBins = 2 * kPlanThreads;   // visit counts 0 .. 2047 (kMaxTilesK = 2048)
 
 // Per query tile: the number of key tiles it will visit (one thread per tile).
 __global__ void __launch_bounds__(256) plan_count(const uint32_t* mask, int n, int W, int Tk,
@@ -72,22 +74,27 @@ __device__ uint32_t plan_exclusive_scan(uint32_t v, uint32_t* s) {
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_order(const uint16_t* count, int n, int Tq,
-                                                           int Tk, int descending,
+                                                           int Tk, int descending, int tail_max,
                                                            uint32_t* perm) {
   __shared__ uint32_t s_scan[kPlanThreads];
-  __shared__ unsigned long long s_work[kPlanHeads];   // remaining work per head
-  __shared__ uint32_t s_pre[kPlanHeads + 1];          // other tiles before each head's first
+  __shared__ uint32_t s_hist[kPlanBins];              // counts of the non-heavy tiles
+  __shared__ unsigned long long s_work[kPlanHeads];   // middle work per head
+  __shared__ uint32_t s_pre[kPlanHeads + 1];          // middle tiles before each head's first
   __shared__ uint32_t s_base[kPlanHeads];             // rank -> head, then head -> first position
   __shared__ unsigned long long s_total;
-  __shared__ uint32_t s_heavy;
+  __shared__ uint32_t s_heavy, s_cut, s_short;
   const int t = threadIdx.x;
   const int heads = n / Tq;
   const bool by_work = heads <= kPlanHeads;
   // every thread walks a contiguous range of tiles (natural order) in each pass
   const int per = (n + kPlanThreads - 1) / kPlanThreads;
   const int lo = min(n, t * per), hi = min(n, lo + per);
-  if (t == 0) s_total = 0ull;
+  if (t == 0) {
+    s_total = 0ull;
+    s_cut = 0u;
+  }
   for (int h = t; h < kPlanHeads; h += kPlanThreads) s_work[h] = 0ull;
+  for (int c = t; c < kPlanBins; c += kPlanThreads) s_hist[c] = 0u;
   __syncthreads();
   unsigned long long sum = 0ull;
   for (int x = lo; x < hi; ++x) sum += count[x];
@@ -98,21 +105,56 @@ __global__ void __launch_bounds__(kPlanThreads) plan_order(const uint16_t* count
   auto heavy = [&](int c) {
     return 2 * c >= Tk && (unsigned long long)c * (unsigned long long)n >= 4ull * total;
   };
-  // 1. heavy tiles in natural order
+  // 1. heavy tiles in natural order; histogram of the others' counts
   uint32_t nh = 0u;
-  for (int x = lo; x < hi; ++x) nh += heavy(count[x]) ? 1u : 0u;
+  for (int x = lo; x < hi; ++x) {
+    const int c = count[x];
+    if (heavy(c)) ++nh;
+    else if (c < kPlanBins) atomicAdd(&s_hist[c], 1u);
+  }
   uint32_t at = plan_exclusive_scan(nh, s_scan);
   if (t == kPlanThreads - 1) s_heavy = at + nh;
   for (int x = lo; x < hi; ++x)
     if (heavy(count[x])) perm[at++] = (uint32_t)x;
-  // 2. the other tiles: their natural-order prefix count, per-head starts and work
-  uint32_t pre = plan_exclusive_scan((uint32_t)(hi - lo) - nh, s_scan);
-  const uint32_t pre_lo = pre;
   __syncthreads();
   const uint32_t n_heavy = s_heavy;
+  // the cut: the largest c whose tiles below it number at most k
+  const uint32_t k = min((uint32_t)max(tail_max, 0), ((uint32_t)n - n_heavy) / 4u);
+  {
+    const uint32_t h0 = s_hist[2 * t], h1 = s_hist[2 * t + 1];
+    const uint32_t below = plan_exclusive_scan(h0 + h1, s_scan);   // tiles with count < 2t
+    uint32_t cut = 0u;
+    if (below <= k) cut = 2u * t;
+    if (below + h0 <= k) cut = 2u * t + 1u;
+    if (t == kPlanThreads - 1 && below + h0 + h1 <= k) cut = kPlanBins;
+    atomicMax(&s_cut, cut);
+  }
+  __syncthreads();
+  const int cut = (int)s_cut;
+  auto is_short = [&](int c) { return c < cut && !heavy(c); };
+  // 3. short tiles last, in traversal order
+  uint32_t ns = 0u, nm = 0u;
+  for (int x = lo; x < hi; ++x) {
+    const int c = count[x];
+    if (is_short(c)) ++ns;
+    else if (!heavy(c)) ++nm;
+  }
+  uint32_t sp = plan_exclusive_scan(ns, s_scan);
+  if (t == kPlanThreads - 1) s_short = sp + ns;
+  __syncthreads();
+  const uint32_t n_short = s_short;
+  for (int x = lo; x < hi; ++x)
+    if (is_short(count[x])) {
+      const uint32_t idx = sp++;
+      perm[(uint32_t)n - n_short + (descending ? n_short - 1u - idx : idx)] = (uint32_t)x;
+    }
+  auto middle = [&](int c) { return !heavy(c) && !is_short(c); };
+  // 2. the middle tiles: their natural-order prefix count, per-head starts and work
+  uint32_t pre = plan_exclusive_scan(nm, s_scan);
+  const uint32_t pre_lo = pre;
   if (!by_work) {   // natural head order
     for (int x = lo; x < hi; ++x)
-      if (!heavy(count[x])) perm[n_heavy + pre++] = (uint32_t)x;
+      if (middle(count[x])) perm[n_heavy + pre++] = (uint32_t)x;
     return;
   }
   {
@@ -127,7 +169,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_order(const uint16_t* count
       }
       if (x == h * Tq) s_pre[h] = pre;
       const int c = count[x];
-      if (!heavy(c)) {
+      if (middle(c)) {
         w += (unsigned long long)c;
         ++pre;
       }
@@ -157,10 +199,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_order(const uint16_t* count
   const uint32_t before = plan_exclusive_scan(my_rest, s_scan);
   if (t < heads) s_base[my_head] = n_heavy + before;   // head -> first position
   __syncthreads();
-  // 3. each head's other tiles in the direction of the step's key traversal
+  // each head's middle tiles in the direction of the step's key traversal
   pre = pre_lo;
   for (int x = lo; x < hi; ++x) {
-    if (heavy(count[x])) continue;
+    if (!middle(count[x])) continue;
     const int h = x / Tq;
     const uint32_t within = pre++ - s_pre[h];
     const uint32_t rest = s_pre[h + 1] - s_pre[h];
@@ -242,7 +284,7 @@ size_t plan_workspace_bytes(int64_t n_tiles) {
 }
 
 hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk, int descending,
-                       void* workspace, hipStream_t stream) {
+                       int tail_max, void* workspace, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   uint32_t* perm = static_cast<uint32_t*>(workspace);
   uint16_t* count = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) +
@@ -253,7 +295,7 @@ hipError_t launch_plan(const uint32_t* mask, int n_tiles, int Tq, int W, int Tk,
                                  stream);
   if (e != hipSuccess) return e;
   const uint16_t* ccount = count;
-  void* args[] = {&ccount, &n_tiles, &Tq, &Tk, &descending, &perm};
+  void* args[] = {&ccount, &n_tiles, &Tq, &Tk, &descending, &tail_max, &perm};
   return hipLaunchKernel(reinterpret_cast<const void*>(&plan_order), dim3(1),
                          dim3(kPlanThreads), args, 0, stream);
 }

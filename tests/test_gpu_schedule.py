@@ -1,6 +1,7 @@
 """Scheduled steps (lite_attn_step_scheduled): the same results as lite_attn_step, bit for bit,
-and the documented tile order (heavy query tiles first in natural order, then the other tiles
-head by head, heads by decreasing work, each head in the step's traversal direction)."""
+and the documented tile order (heavy query tiles first in natural order, then the middle tiles
+head by head, heads by decreasing work, each head in the step's traversal direction, then the
+short tiles in traversal order)."""
 import numpy as np
 import pytest
 import torch
@@ -12,24 +13,44 @@ from workloads import Workload, derive, get_config
 pytestmark = pytest.mark.gpu
 
 
-def expected_order(mask_np: np.ndarray, tiles_k: int, tiles_q: int, descending: bool) -> np.ndarray:
-    """Reference tile order for a mask [B, H, Tq, W]: tiles visiting at least half of all key
-    tiles and at least four times the mean first, in natural order; then, head by head, heads by
-    decreasing work left (sum of their other tiles' visit counts; ties by index), each head's
-    other tiles in the direction of the step's key traversal."""
+def tail_max() -> int:
+    """Short tiles the library puts last at most: eight per workgroup slot, two slots per CU."""
+    return 16 * torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def expected_order(mask_np: np.ndarray, tiles_k: int, tiles_q: int, descending: bool,
+                   tail: int) -> np.ndarray:
+    """Reference tile order for a mask [B, H, Tq, W]:
+    - heavy tiles (visiting at least half of all key tiles and at least four times the mean)
+      first, in natural order;
+    - short tiles last: the non-heavy tiles with a visit count below the largest cut c that
+      leaves at most min(tail, non-heavy // 4) of them (counts of 2048 are never short), in the
+      step's traversal order (natural order, reversed on descending steps);
+    - between them the middle tiles, head by head, heads by decreasing middle work (sum of their
+      visit counts; ties by index), each head's tiles in the direction of the step's key
+      traversal (natural head order above 1024 heads)."""
     bits = mask_to_bits(mask_np, tiles_k).reshape(-1, tiles_k)
     count = (tiles_k - bits.sum(axis=1)).astype(np.int64)
     n = count.size
     heavy = (2 * count >= tiles_k) & (count * n >= 4 * count.sum())
+    k = min(tail, (n - int(heavy.sum())) // 4)
+    rest = count[~heavy]
+    rest = rest[rest < 2048]
+    cut = max(c for c in range(2049) if int((rest < c).sum()) <= k)
+    short = ~heavy & (count < cut)
+    middle = ~heavy & ~short
     order = list(np.nonzero(heavy)[0])
     heads = n // tiles_q
     if heads > 1024:
-        return np.array(order + list(np.nonzero(~heavy)[0]))
-    work = [int(count[h * tiles_q:(h + 1) * tiles_q][~heavy[h * tiles_q:(h + 1) * tiles_q]].sum())
-            for h in range(heads)]
-    for h in sorted(range(heads), key=lambda h: (-work[h], h)):
-        rows = range(tiles_q - 1, -1, -1) if descending else range(tiles_q)
-        order += [h * tiles_q + i for i in rows if not heavy[h * tiles_q + i]]
+        order += list(np.nonzero(middle)[0])
+    else:
+        work = [int(count[h * tiles_q:(h + 1) * tiles_q][middle[h * tiles_q:(h + 1) * tiles_q]].sum())
+                for h in range(heads)]
+        for h in sorted(range(heads), key=lambda h: (-work[h], h)):
+            rows = range(tiles_q - 1, -1, -1) if descending else range(tiles_q)
+            order += [h * tiles_q + i for i in rows if middle[h * tiles_q + i]]
+    tail_tiles = list(np.nonzero(short)[0])
+    order += tail_tiles[::-1] if descending else tail_tiles
     return np.array(order)
 
 
@@ -61,7 +82,8 @@ def test_scheduled_step_matches_plain_step(label, cid, kw, steps):
         assert torch.equal(m_plain, m_sched), f"{label} step {t}: masks differ"
         perm = ws[:4 * n].view(torch.int32).cpu().numpy()
         desc = cfg.order == "alt" and t % 2 == 1
-        assert np.array_equal(perm, expected_order(start, tk, tq, desc)), f"{label} step {t}: order"
+        assert np.array_equal(perm, expected_order(start, tk, tq, desc, tail_max())), \
+            f"{label} step {t}: order"
         log(f"  [{label}] step {t}: first tiles {perm[:6].tolist()}")
 
 
@@ -89,7 +111,7 @@ def test_scheduled_full_size_order_and_result():
     assert torch.equal(o1, o2) and torch.equal(m1, m2)
     n = cfg.batch * cfg.heads * tq
     perm = ws[:4 * n].view(torch.int32).cpu().numpy()
-    assert np.array_equal(perm, expected_order(start, tk, tq, False))
+    assert np.array_equal(perm, expected_order(start, tk, tq, False, tail_max()))
     # the prefix query tiles (rows [0, 256) of every head) are never skipped, so in a sparse
     # step they are heavy and run first
     bits = mask_to_bits(start, tk).reshape(-1, tk)
