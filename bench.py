@@ -60,7 +60,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--per-step", action="store_true", help="add per-step times to the JSON")
     ap.add_argument("--schedule", action="store_true",
-                    help="use lite_attn_step_scheduled (heaviest-first query-tile order; the "
+                    help="use lite_attn_step_scheduled (query tiles by visit count: heavy first, short "
+                         "last; the "
                          "scheduling kernel is inside the timed step)")
     ap.add_argument("--refresh-delta", type=float, default=None,
                     help="use lite_attn_step_refresh with this divergence budget (mask rows whose "

@@ -187,9 +187,10 @@ int lite_attn_step_refresh(lite_attn_t handle, const void* q, const void* k, con
  * 256-byte units (0 for a NULL handle). */
 size_t lite_attn_workspace_bytes(lite_attn_t handle);
 
-/* lite_attn_step with a heaviest-first schedule: same arguments, same results (bit for bit),
- * plus a caller-owned device `workspace` of lite_attn_workspace_bytes(handle) bytes, 256-byte
- * aligned, that the call overwrites (it holds nothing between calls). A first kernel reads the
+/* lite_attn_step with a schedule from the tiles' visit counts (heavy first, short last): same
+ * arguments, same results (bit for bit), plus a caller-owned device `workspace` of
+ * lite_attn_workspace_bytes(handle) bytes, 256-byte aligned, that the call overwrites (it holds
+ * nothing between calls). A first kernel reads the
  * mask and counts, per query tile, the key tiles it will visit (its skip-list length). Query
  * tiles that visit at least half of all key tiles and at least four times the mean (dense
  * prefix rows in a sparse step, for example) are scheduled first. The shortest tiles go last,

@@ -74,7 +74,8 @@ class LiteAttention:
         lite_attn_reset_mask(self.handle, mask, stream)
 
     def new_workspace(self, device):
-        """Device workspace for scheduled steps (heaviest-first query-tile order)."""
+        """Device workspace for scheduled steps (query tiles ordered by visit count: heavy first,
+        short last)."""
         import torch
         return torch.empty(max(1, lite_attn_workspace_bytes(self.handle)), dtype=torch.uint8,
                            device=device)
@@ -88,7 +89,7 @@ class LiteAttention:
 
     def step(self, q, k, v, out, mask, log_eps_t: float, step: int, stream=None, workspace=None,
              tile_stats=None, refresh_delta: float = float("inf")):
-        """One denoising step. With a workspace the query tiles run heaviest first; with
+        """One denoising step. With a workspace the query tiles run heavy first and short last; with
         tile_stats the mask rows whose statistic moved by more than refresh_delta are cleared
         (divergence refresh). The two options are separate entry points and do not combine."""
         if tile_stats is not None:

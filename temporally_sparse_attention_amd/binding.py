@@ -342,7 +342,7 @@ def lite_attn_workspace_bytes(handle: Handle) -> int:
 
 def lite_attn_step_scheduled(handle: Handle, q, k, v, out, mask, log_eps_t: float, step: int,
                              workspace, stream=None):
-    """lite_attn_step with a heaviest-first schedule; `workspace` is a device tensor of at least
+    """lite_attn_step with a visit-count schedule (heavy tiles first, short last); `workspace` is a device tensor of at least
     lite_attn_workspace_bytes(handle) bytes, 256-byte aligned."""
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _check_qkvo(handle, t, name)
