@@ -49,10 +49,13 @@ def test_in_step_dtype_headdim_variants(dtype_name, d):
                          in_step_skip=True)
 
 
-def test_in_step_full_size_sampled_parity():
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_in_step_full_size_sampled_parity(cid):
+    """Every step of each bf16 workload's schedule at full size, on sampled query tiles (with
+    the HunyuanVideo shape's dense-prefix tiles and the stress shape's D = 64)."""
     dev = device()
-    cfg = get_config(3)
-    rows = _sample_rows(cfg, np.random.default_rng(33), n_heads=2, per_head=2)
+    cfg = get_config(cid)
+    rows = _sample_rows(cfg, np.random.default_rng(33 + cid), n_heads=2, per_head=2)
     log(f"== in-step {cfg.name} full size, {len(rows)} sampled query tiles, {cfg.steps} steps")
     wl = Workload(cfg, dev)
     teacher_forced_chain(cfg, wl, cfg.steps, rows=rows, label="ins-" + cfg.name,

@@ -11,6 +11,7 @@ import torch
 
 from gpu_util import (MARGIN_BAND, OUT_MAX, OUT_MEAN, device, from_mask_tensor, log,
                       make_attention, to_mask_tensor)
+from test_gpu_parity import _sample_rows
 from oracle import lite_attn_step_ref, mask_to_bits
 from workloads import Workload, derive, get_config
 
@@ -98,3 +99,79 @@ def test_refresh_clears_rows_when_attention_moves():
         return q, k, v
     n = refresh_chain(cfg, wl, 4, 1.0, inputs=inputs, label="rf-roll")
     assert n > 0
+
+
+def test_refresh_full_size_sampled_parity():
+    """The 75600-token workload over its whole schedule at full size, teacher-forced on sampled
+    query tiles: before each step the sampled tiles' mask rows and references are set to the
+    oracle's (the others keep the GPU's own), and the sampled outputs, mask rows and statistics
+    are compared as in the small cases."""
+    dev = device()
+    cfg = get_config(3)
+    delta = 0.2
+    att = make_attention(cfg)
+    tq, tk = att.tiles
+    B, H = cfg.batch, cfg.heads
+    rows = _sample_rows(cfg, np.random.default_rng(77), n_heads=2, per_head=2)
+    sel = np.zeros((B, H, tq), dtype=bool)
+    for (b, h, i) in rows:
+        sel[b, h, i] = True
+    heads = sorted({(b, h) for (b, h, _) in rows})
+    log(f"== refresh {cfg.name} full size, {len(rows)} sampled query tiles, delta {delta}")
+    wl = Workload(cfg, dev)
+    ref_mask = np.zeros(att.mask_shape, dtype=np.uint32)
+    ref_stats = np.full((B, H, tq), np.nan)
+    gmask = att.new_mask(dev)
+    gstats = att.new_tile_stats(dev)
+    worst, total, n_el, refreshed = 0.0, 0.0, 0, 0
+    for t in range(cfg.steps):
+        le = cfg.log_eps[t]
+        q, k, v = wl.inputs(t)
+        out = torch.full_like(q, float("nan"))
+        cur = from_mask_tensor(gmask)
+        cur[sel] = ref_mask[sel]
+        gmask.copy_(to_mask_tensor(cur, dev))
+        gs = gstats.cpu().numpy()
+        gs[sel] = ref_stats[sel]
+        gstats.copy_(torch.from_numpy(gs.astype(np.float32)).to(dev))
+        att.step(q, k, v, out, gmask, le, t, tile_stats=gstats, refresh_delta=delta)
+        torch.cuda.synchronize()
+        gbits_all = mask_to_bits(from_mask_tensor(gmask), tk)
+        gstats_all = gstats.double().cpu().numpy()
+        gout = out
+        for (b, h) in heads:
+            tiles = [i for (bb, hh, i) in rows if (bb, hh) == (b, h)]
+            r = lite_attn_step_ref(q[b:b + 1, h:h + 1].cpu(), k[b:b + 1, h:h + 1].cpu(),
+                                   v[b:b + 1, h:h + 1].cpu(), ref_mask[b:b + 1, h:h + 1],
+                                   tile_q=cfg.tile_q, tile_k=cfg.tile_k,
+                                   softmax_scale=cfg.softmax_scale, log_eps=le, step=t,
+                                   order=cfg.order, dense_prefix=cfg.dense_prefix,
+                                   rows=[(0, 0, i) for i in tiles],
+                                   tile_stats=ref_stats[b:b + 1, h:h + 1], refresh_delta=delta)
+            for i in tiles:
+                r0, r1 = i * cfg.tile_q, min(cfg.seq_len, (i + 1) * cfg.tile_q)
+                d = np.abs(gout[b, h, r0:r1].double().cpu().numpy() - r.out[0, 0, r0:r1])
+                worst = max(worst, float(d.max()))
+                total += float(d.sum())
+                n_el += d.size
+                move = abs(r.stats[0, 0, i] - ref_stats[b, h, i])
+                near_refresh = abs(move - delta) <= 1e-3 * max(1.0, abs(r.stats[0, 0, i]))
+                near_margin = np.abs(np.nan_to_num(r.margins[0, 0, i], nan=np.inf)) <= MARGIN_BAND
+                rbits = mask_to_bits(r.mask_next[0:1, 0:1, i:i + 1], tk)[0, 0, 0]
+                bad = (gbits_all[b, h, i] != rbits) & ~near_margin & ~near_refresh
+                assert not bad.any(), f"step {t} tile {(b, h, i)}: {int(bad.sum())} bits differ"
+                want, got = r.stats_next[0, 0, i], gstats_all[b, h, i]
+                ok = (np.isnan(want) and np.isnan(got)) or near_refresh or \
+                    abs(got - want) <= 1e-3 * max(1.0, abs(want))
+                assert ok, f"step {t} tile {(b, h, i)}: statistic {got} against {want}"
+                ref_mask[b, h, i] = r.mask_next[0, 0, i]
+                ref_stats[b, h, i] = r.stats_next[0, 0, i]
+                refreshed += int(r.refreshed[0, 0, i])
+        log(f"  [refresh-{cfg.name}] step {t}: skipped(next, sampled) "
+            f"{mask_to_bits(ref_mask, tk)[sel].mean():.3f} refreshed so far {refreshed} "
+            f"max|d| so far {worst:.2e}")
+    mean = total / max(1, n_el)
+    log(f"[refresh-{cfg.name}] out max|d|={worst:.3e} mean|d|={mean:.3e} refreshed={refreshed}")
+    assert worst <= OUT_MAX and mean <= OUT_MEAN
+    wl.drop_cache()
+    torch.cuda.empty_cache()
