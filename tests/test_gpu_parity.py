@@ -98,8 +98,30 @@ def test_full_size_sampled_parity(cid, steps):
     torch.cuda.empty_cache()
 
 
+# Launch variants the five workloads do not use at full size: tile_q 64 (the D = 128 one runs
+# through the one-tile-per-call driver, the D = 64 one has 2 waves per workgroup), and the
+# ascending order over a whole schedule.
+VARIANTS = [
+    ("wan2.1_1.3b_tq64", 2, dict(tile_q=64)),
+    ("stress_edge_tq64", 5, dict(tile_q=64)),
+    ("wan14b_720p_asc", 3, dict(order="asc")),
+]
+
+
+@pytest.mark.parametrize("label,cid,kw", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_full_size_launch_variants(label, cid, kw):
+    dev = device()
+    cfg = derive(get_config(cid), name=label, **kw)
+    rows = _sample_rows(cfg, np.random.default_rng(100 + cid), n_heads=2, per_head=2)
+    log(f"== {label} full size N={cfg.seq_len}, {len(rows)} sampled query tiles, {cfg.steps} steps")
+    wl = Workload(cfg, dev)
+    teacher_forced_chain(cfg, wl, cfg.steps, rows=rows, label=label)
+    wl.drop_cache()
+    torch.cuda.empty_cache()
+
+
 def test_full_size_scheduled_parity_with_dense_prefix():
-    """lite_attn_step_scheduled (heaviest-first order from the visit counts, caller workspace)
+    """lite_attn_step_scheduled (order from the visit counts, caller workspace)
     against the oracle over the whole HunyuanVideo-shaped schedule, on sampled query tiles that
     include the dense-prefix rows, which the schedule moves to the front."""
     dev = device()
