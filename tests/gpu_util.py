@@ -85,10 +85,12 @@ def make_attention(cfg, **over):
 
 
 def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=None,
-                         scale=None, label="", log_eps=None, in_step_skip=False, workspace=None):
+                         scale=None, label="", log_eps=None, in_step_skip=False, workspace=None,
+                         make_out=None):
     """Run `steps` steps. Before each step the GPU mask rows under test are overwritten with
     the oracle's mask; outputs and new mask rows are compared on `rows` (default: all). With a
-    workspace the GPU runs the scheduled step (lite_attn_step_scheduled)."""
+    workspace the GPU runs the scheduled step (lite_attn_step_scheduled). make_out(q) allocates
+    the output (default: a NaN-filled tensor like q)."""
     dev = workload.device
     order = order or cfg.order
     scale = cfg.softmax_scale if scale is None else scale
@@ -106,7 +108,7 @@ def teacher_forced_chain(cfg, workload, steps, *, rows=None, att=None, order=Non
     for t in range(steps):
         le = cfg.log_eps[t] if log_eps is None else log_eps[t]
         q, k, v = workload.inputs(t)
-        out = torch.full_like(q, float("nan"))
+        out = make_out(q) if make_out is not None else torch.full_like(q, float("nan"))
         if sel is None:
             gpu_mask.copy_(to_mask_tensor(ref_mask, dev))
         else:

@@ -120,6 +120,53 @@ def test_full_size_launch_variants(label, cid, kw):
     torch.cuda.empty_cache()
 
 
+class _PackedInputs:
+    """A workload's step inputs as views of one packed [B, N, 3, H, D] tensor (a fused QKV
+    projection: stride_n = 3HD, stride_h = D), copied from the contiguous ones."""
+
+    def __init__(self, wl):
+        self.wl, self.device, self.buf = wl, wl.device, None
+
+    def inputs(self, t):
+        xs = self.wl.inputs(t)
+        B, H, N, D = xs[0].shape
+        if self.buf is None:
+            self.buf = torch.empty(B, N, 3, H, D, dtype=xs[0].dtype, device=self.device)
+        views = tuple(self.buf[:, :, c].permute(0, 2, 1, 3) for c in range(3))
+        for view, x in zip(views, xs):
+            view.copy_(x)
+        return views
+
+
+def test_full_size_strided_parity():
+    """The Wan2.1-1.3B-shaped schedule at full size with q, k, v (and out) as strided views of
+    packed [B, N, 3, H, D] tensors: one head spans about 300 MB, so every K/V tile offset is
+    large. Nothing is written outside out's view."""
+    dev = device()
+    cfg = get_config(2)
+    wl = Workload(cfg, dev)
+    packed = _PackedInputs(wl)
+    q0 = packed.inputs(0)[0]
+    st = q0.stride()
+    att = make_attention(cfg, strides=(st[0], st[1], st[2]))
+    B, H, N, D = q0.shape
+    out_bufs = []
+
+    def make_out(q):
+        full = torch.full((B, N, 3, H, D), float("nan"), dtype=q.dtype, device=dev)
+        out_bufs.append(full)
+        return full[:, :, 0].permute(0, 2, 1, 3)
+
+    rows = _sample_rows(cfg, np.random.default_rng(202), n_heads=2, per_head=2)
+    log(f"== strided {cfg.name} full size, strides {st}, {len(rows)} sampled query tiles")
+    teacher_forced_chain(cfg, packed, cfg.steps, rows=rows, att=att, label="strided-" + cfg.name,
+                         make_out=make_out)
+    for full in out_bufs:
+        assert torch.isnan(full[:, :, 1:].float()).all()   # nothing written outside out
+    wl.drop_cache()
+    torch.cuda.empty_cache()
+
+
 def test_full_size_scheduled_parity_with_dense_prefix():
     """lite_attn_step_scheduled (order from the visit counts, caller workspace)
     against the oracle over the whole HunyuanVideo-shaped schedule, on sampled query tiles that
